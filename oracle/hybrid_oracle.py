@@ -1,0 +1,144 @@
+"""Plain fp64 CPU oracle of the ARL2 hybrid attention layer.
+
+TEST INFRASTRUCTURE. Only the test suite, the package smoke check and the
+bench's CPU-baseline leg may import this module. The product path never calls
+it and shares no code with it (it does not import the GPU package; it takes
+float64 numpy arrays and nothing else).
+
+Source: "Attend Locally, Remember Linearly" (ARL2, arXiv 2605.16579; the
+gist.science technical summary), section 2.1 (hybrid attention decomposition)
+and section 2.2 (state management). What the layer computes, per stream b and
+head h, for frame N with rows r = [N*L, (N+1)*L):
+
+  intra-frame branch (2.1, item 1): bidirectional softmax attention among the
+      tokens of frame N only, with the frozen Q, K, V;
+  inter-frame branch (2.1, "outputs"): O_inter = Q'_N S_{N-1};
+  state update (2.1, gated update rule):
+      S_N = alpha_N S_{N-1} + K'_N^T diag(beta_N) (V'_N - K'_N S_{N-1});
+  frame-level access (2.2): every token of frame N reads the same S_{N-1};
+      S is written only after the whole frame;
+  clean-pass updates (2.2): denoising passes read S and never write it; only
+      the clean pass writes it (update_state = 1).
+
+Readings where the page is silent or garbled (each is listed in the design doc):
+  * the printed update rule has no transpose and no diag; the only
+    dimensionally valid reading is K'^T diag(beta) (V' - K' S_{N-1}), with the
+    residual taken against the undecayed S_{N-1} exactly as printed;
+  * alpha is one scalar per (stream, frame, head); beta one scalar per
+    (stream, token, head);
+  * the branches combine by a plain sum, O = O_intra + O_inter;
+  * the softmax scale is 1/sqrt(d) unless given; no mask inside a frame;
+  * with update_state = 0 every frame reads the input state.
+
+Every function here is pinned by tests/test_oracle_pins.py against
+properties the page and the mathematics fix (row sums, closed forms, the
+delta-rule recall property, brute force on tiny inputs, textbook attention).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Row-wise softmax of a 2-D fp64 array: exp(z - max) / sum (2.1, item 1)."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def intra_frame_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                          scale: float | None = None) -> np.ndarray:
+    """Bidirectional softmax attention among the L tokens of one frame.
+
+    q, k: [L, d_k], v: [L, d_v] fp64. Returns softmax(q k^T * scale) v, [L, d_v].
+    ARL2 section 2.1 item 1 (the branch keeps the pretrained softmax attention
+    inside each frame, no causal mask).
+    """
+    d = q.shape[1]
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    p = softmax_rows((q @ k.T) * s)
+    return p @ v
+
+
+def inter_frame_readout(qp: np.ndarray, state: np.ndarray) -> np.ndarray:
+    """O_inter = Q'_N S_{N-1}; qp [L, d_k], state [d_k, d_v]. ARL2 2.1 outputs."""
+    return qp @ state
+
+
+def delta_update(state: np.ndarray, kp: np.ndarray, vp: np.ndarray,
+                 alpha: float, beta: np.ndarray) -> np.ndarray:
+    """One gated-delta write of the state after a clean frame (ARL2 2.1).
+
+    S_N = alpha S_{N-1} + K'^T diag(beta) (V' - K' S_{N-1}).
+    state [d_k, d_v], kp [L, d_k], vp [L, d_v], beta [L], alpha scalar.
+    """
+    resid = vp - kp @ state
+    return alpha * state + kp.T @ (beta[:, None] * resid)
+
+
+def hybrid_layer_head(q, k, v, qp, kp, vp, alpha, beta, state, frame_len,
+                      update_state, scale=None, frames=None):
+    """The layer for one (stream, head): all frames in order.
+
+    q..vp: [T, d] fp64; alpha: [F]; beta: [T]; state: [d_k, d_v].
+    frames: optional set of frame indices whose output is wanted (others are
+    returned as NaN); the state chain always runs over every frame.
+    Returns (out [T, d_v], state_after [d_k, d_v]).
+    Frame N reads S_{N-1} (section 2.2, frame-level access); with
+    update_state the state advances after each frame, otherwise it is left
+    as given (section 2.2, clean-pass updates).
+    """
+    T = q.shape[0]
+    L = int(frame_len)
+    F = T // L
+    S = np.array(state, dtype=np.float64, copy=True)
+    out = np.full((T, v.shape[1]), np.nan)
+    for n in range(F):
+        r = slice(n * L, (n + 1) * L)
+        if frames is None or n in frames:
+            out[r] = intra_frame_attention(q[r], k[r], v[r], scale) + inter_frame_readout(qp[r], S)
+        if update_state:
+            S = delta_update(S, kp[r], vp[r], float(alpha[n]), beta[r])
+    return out, S
+
+
+def hybrid_layer(q, k, v, qp, kp, vp, alpha, beta, state, frame_len,
+                 update_state, scale=None):
+    """The whole layer call, all streams and heads.
+
+    q..vp: [B, T, H, d] fp64; alpha: [B, F, H]; beta: [B, T, H];
+    state: [B, H, d_k, d_v]. Returns (out [B, T, H, d_v], state_out).
+    state_out equals state when update_state is 0.
+    """
+    B, T, H, _ = q.shape
+    out = np.empty((B, T, H, v.shape[3]), dtype=np.float64)
+    st = np.array(state, dtype=np.float64, copy=True)
+    for b in range(B):
+        for h in range(H):
+            a = alpha[b, :, h] if alpha is not None else None
+            bt = beta[b, :, h] if beta is not None else None
+            kk = kp[b, :, h] if kp is not None else None
+            vv = vp[b, :, h] if vp is not None else None
+            out[b, :, h], st[b, h] = hybrid_layer_head(
+                q[b, :, h], k[b, :, h], v[b, :, h], qp[b, :, h], kk, vv, a, bt,
+                st[b, h], frame_len, update_state, scale)
+    return out, st
+
+
+def state_chain(kp, vp, alpha, beta, state, frame_len):
+    """Only the state recursion for one (stream, head): S after every frame.
+
+    kp, vp: [T, d]; alpha: [F]; beta: [T]; state: [d, d].
+    Returns the list [S_0 (input), S_1, ..., S_F]. ARL2 2.1 update rule.
+    """
+    L = int(frame_len)
+    F = kp.shape[0] // L
+    S = np.array(state, dtype=np.float64, copy=True)
+    chain = [S]
+    for n in range(F):
+        r = slice(n * L, (n + 1) * L)
+        S = delta_update(S, kp[r], vp[r], float(alpha[n]), beta[r])
+        chain.append(S)
+    return chain

@@ -1,0 +1,307 @@
+"""Pins of the fp64 oracle against what the ARL2 page and the mathematics fix.
+
+Each check_* function raises AssertionError when the oracle it is handed
+disagrees with a property that does not depend on the oracle itself: a
+closed form worked out by hand, a textbook routine, brute force written with
+scalar loops, or an invariant of the method ("Attend Locally, Remember
+Linearly", section 2.1 update rule and readout, section 2.2 access rules).
+The checks take the oracle module as an argument so that
+tests/test_oracle_mutants.py can hand them deliberately broken copies.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _unit_rows(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _inputs(rng, B=1, T=12, H=2, d=4, L=4, alpha=None, beta=None, S0=None):
+    F = T // L
+    q, k, v, qp, kp, vp = (_rand(rng, B, T, H, d) for _ in range(6))
+    kp = _unit_rows(kp)
+    a = rng.uniform(0.6, 0.99, (B, F, H)) if alpha is None else np.full((B, F, H), float(alpha))
+    b = rng.uniform(0.01, 0.3, (B, T, H)) if beta is None else np.full((B, T, H), float(beta))
+    s = 0.3 * _rand(rng, B, H, d, d) if S0 is None else S0
+    return q, k, v, qp, kp, vp, a, b, s
+
+
+# --- brute force with scalar loops (independent of numpy linear algebra) ------
+
+def brute_layer_head(q, k, v, qp, kp, vp, alpha, beta, S, L, update, scale):
+    """The layer for one head, written with Python scalar loops only."""
+    T, d = len(q), len(q[0])
+    S = [[float(S[i][j]) for j in range(d)] for i in range(d)]
+    out = [[0.0] * d for _ in range(T)]
+    for n in range(T // L):
+        rows = range(n * L, (n + 1) * L)
+        for i in rows:
+            scores = [sum(q[i][c] * k[j][c] for c in range(d)) * scale for j in rows]
+            m = max(scores)
+            w = [math.exp(z - m) for z in scores]
+            tot = sum(w)
+            for c in range(d):
+                intra = sum(w[jj] * v[j][c] for jj, j in enumerate(rows)) / tot
+                inter = sum(qp[i][r] * S[r][c] for r in range(d))
+                out[i][c] = intra + inter
+        if update:
+            a = float(alpha[n])
+            newS = [[a * S[r][c] for c in range(d)] for r in range(d)]
+            for t in rows:
+                for c in range(d):
+                    resid = vp[t][c] - sum(kp[t][r] * S[r][c] for r in range(d))
+                    for r in range(d):
+                        newS[r][c] += kp[t][r] * beta[t] * resid
+            S = newS
+    return np.array(out), np.array(S)
+
+
+# --- the checks ---------------------------------------------------------------
+
+def check_softmax_rows_sum_to_one(o):
+    rng = np.random.default_rng(1)
+    z = 4.0 * _rand(rng, 37, 53)
+    p = o.softmax_rows(z)
+    assert np.all(p > 0) and np.all(p <= 1)
+    assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-12
+    # two-element closed form: softmax([a, b]) = [1/(1+e^(b-a)), 1/(1+e^(a-b))]
+    p2 = o.softmax_rows(np.array([[0.3, -1.2]]))
+    assert abs(p2[0, 0] - 1.0 / (1.0 + math.exp(-1.5))) < 1e-15
+    assert abs(p2[0, 1] - 1.0 / (1.0 + math.exp(1.5))) < 1e-15
+
+
+def check_hand_worked_example(o):
+    """Two frames of two tokens, d = 2, every value worked out by hand."""
+    e = math.e
+    I = np.eye(2)
+    q = np.zeros((1, 4, 1, 2)); k = np.zeros_like(q); v = np.zeros_like(q)
+    qp = np.zeros_like(q); kp = np.zeros_like(q); vp = np.zeros_like(q)
+    # frame 0: Q = K = I, V = [[1,2],[3,4]], Q' = [[1,1],[0,2]], K' = I,
+    #          V' = [[2,3],[4,5]], beta = (0.5, 0.25), alpha = 0.5, S0 = I
+    q[0, 0:2, 0] = I; k[0, 0:2, 0] = I; v[0, 0:2, 0] = [[1, 2], [3, 4]]
+    qp[0, 0:2, 0] = [[1, 1], [0, 2]]; kp[0, 0:2, 0] = I; vp[0, 0:2, 0] = [[2, 3], [4, 5]]
+    # frame 1: Q = K = 0 (uniform softmax), V = [[2,0],[0,2]], Q' = I
+    v[0, 2:4, 0] = [[2, 0], [0, 2]]; qp[0, 2:4, 0] = I; kp[0, 2:4, 0] = I
+    alpha = np.array([[[0.5], [1.0]]])
+    beta = np.zeros((1, 4, 1)); beta[0, 0:2, 0] = [0.5, 0.25]
+    S0 = I.reshape(1, 1, 2, 2).copy()
+    out, S = o.hybrid_layer(q, k, v, qp, kp, vp, alpha, beta, S0, 2, 1, scale=1.0)
+    # frame 0 intra: softmax of the identity score matrix
+    w0 = np.array([[e / (e + 1), 1 / (e + 1)], [1 / (e + 1), e / (e + 1)]])
+    intra0 = w0 @ np.array([[1.0, 2.0], [3.0, 4.0]])
+    want0 = intra0 + np.array([[1.0, 1.0], [0.0, 2.0]])          # + Q' S0
+    # S1 = 0.5 I + diag(0.5, 0.25) ([[2,3],[4,5]] - I) = [[1, 1.5], [1, 1.5]]
+    S1 = np.array([[1.0, 1.5], [1.0, 1.5]])
+    want1 = np.array([[1.0, 1.0], [1.0, 1.0]]) + S1                 # uniform avg of V + I S1
+    assert np.max(np.abs(out[0, 0:2, 0] - want0)) < 1e-14
+    assert np.max(np.abs(out[0, 2:4, 0] - want1)) < 1e-14
+    # frame 1 has beta = 0 and alpha = 1: S2 = S1
+    assert np.max(np.abs(S[0, 0] - S1)) < 1e-14
+
+
+def check_single_frame_is_textbook_attention(o):
+    """F = 1, S0 = 0: the layer is plain softmax(QK^T/sqrt(d))V (2.1 item 1)."""
+    import torch
+    rng = np.random.default_rng(2)
+    B, L, H, d = 2, 9, 3, 5
+    q, k, v, qp, kp, vp, a, b, _ = _inputs(rng, B, L, H, d, L)
+    S0 = np.zeros((B, H, d, d))
+    out, _ = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, S0, L, 0)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def check_brute_force_tiny(o):
+    """The whole layer against scalar-loop brute force, 3 frames, update on."""
+    rng = np.random.default_rng(3)
+    B, H, d, L, F = 1, 2, 3, 3, 3
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, B, F * L, H, d, L)
+    out, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, L, 1, scale=0.7)
+    for h in range(H):
+        ro, rs = brute_layer_head(q[0, :, h].tolist(), k[0, :, h].tolist(), v[0, :, h].tolist(),
+                                  qp[0, :, h].tolist(), kp[0, :, h].tolist(), vp[0, :, h].tolist(),
+                                  a[0, :, h], b[0, :, h], s[0, h], L, True, 0.7)
+        assert np.max(np.abs(out[0, :, h] - ro)) < 1e-12
+        assert np.max(np.abs(S[0, h] - rs)) < 1e-12
+
+
+def check_alpha1_beta0_keeps_state(o):
+    """alpha = 1, beta = 0: S_N = S_{N-1} exactly and O_inter = Q' S_0 always."""
+    rng = np.random.default_rng(4)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 12, 2, 4, 4, alpha=1.0, beta=0.0)
+    out, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    assert np.array_equal(S, s)
+    out0, _ = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 0)
+    assert np.max(np.abs(out - out0)) == 0.0
+
+
+def check_alpha0_beta0_clears_state(o):
+    """alpha = 0, beta = 0: S_1 = 0, so frames >= 1 get no inter-frame term."""
+    rng = np.random.default_rng(5)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 12, 2, 4, 4, alpha=0.0, beta=0.0)
+    out, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    assert np.all(S == 0.0)
+    zero = np.zeros_like(s)
+    out_z, _ = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, zero, 4, 0)
+    assert np.max(np.abs(out[:, 4:] - out_z[:, 4:])) < 1e-14
+    # frame 0 still reads S_0: its output differs from the S_0 = 0 output by Q' S_0
+    diff = out[0, 0:4, 0] - out_z[0, 0:4, 0]
+    assert np.max(np.abs(diff - qp[0, 0:4, 0] @ s[0, 0])) < 1e-13
+
+
+def check_beta0_geometric_decay(o):
+    """beta = 0: S_F = (prod alpha_n) S_0 (closed form)."""
+    rng = np.random.default_rng(6)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 20, 2, 4, 4, beta=0.0)
+    _, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    for h in range(2):
+        want = np.prod(a[0, :, h]) * s[0, h]
+        assert np.max(np.abs(S[0, h] - want)) < 1e-14
+
+
+def check_delta_rule_recall(o):
+    """Orthonormal K' rows, beta = 1: with alpha = 1 the written state recalls
+    V' exactly (K' S_N = V'); with alpha < 1 the printed rule gives
+    K' S_N = V' - (1 - alpha) K' S_{N-1} (residual against the undecayed state)."""
+    rng = np.random.default_rng(7)
+    L, d = 32, 64
+    Qm, _ = np.linalg.qr(rng.standard_normal((d, L)))
+    kp = Qm.T                                   # [L, d], orthonormal rows
+    vp = rng.standard_normal((L, d))
+    S_prev = rng.standard_normal((d, d))
+    beta = np.ones(L)
+    S1 = o.delta_update(S_prev, kp, vp, 1.0, beta)
+    assert np.max(np.abs(kp @ S1 - vp)) < 1e-12
+    S2 = o.delta_update(S_prev, kp, vp, 0.6, beta)
+    assert np.max(np.abs(kp @ S2 - (vp - 0.4 * kp @ S_prev))) < 1e-12
+    # directions orthogonal to the written keys only decay
+    null = np.linalg.qr(np.concatenate([kp.T, rng.standard_normal((d, d - L))], axis=1))[0][:, L:]
+    assert np.max(np.abs(null.T @ S2 - 0.6 * null.T @ S_prev)) < 1e-12
+
+
+def check_affine_form(o):
+    """S_N = (alpha I - K'^T diag(beta) K') S_{N-1} + K'^T diag(beta) V'."""
+    rng = np.random.default_rng(8)
+    L, d = 40, 16
+    kp = _unit_rows(rng.standard_normal((L, d))); vp = rng.standard_normal((L, d))
+    S = rng.standard_normal((d, d)); beta = rng.uniform(0, 1, L)
+    A = 0.8 * np.eye(d) - kp.T @ np.diag(beta) @ kp
+    Bm = kp.T @ np.diag(beta) @ vp
+    assert np.max(np.abs(o.delta_update(S, kp, vp, 0.8, beta) - (A @ S + Bm))) < 1e-12
+
+
+def check_column_separability(o):
+    """Column j of V' only moves column j of S and of later O_inter."""
+    rng = np.random.default_rng(9)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 12, 1, 4, 4)
+    out, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    vp2 = vp.copy(); vp2[0, :, 0, 2] += 1.0
+    out2, S2 = o.hybrid_layer(q, k, v, qp, kp, vp2, a, b, s, 4, 1)
+    other = [0, 1, 3]
+    assert np.max(np.abs(S2[0, 0][:, other] - S[0, 0][:, other])) < 1e-14
+    assert np.max(np.abs(S2[0, 0][:, 2] - S[0, 0][:, 2])) > 1e-3
+    assert np.max(np.abs(out2[..., other] - out[..., other])) < 1e-14
+    assert np.max(np.abs(out2[0, 4:, 0, 2] - out[0, 4:, 0, 2])) > 1e-4
+
+
+def check_token_permutation(o):
+    """Permuting the tokens of a frame permutes its output rows; S is invariant."""
+    rng = np.random.default_rng(10)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 12, 2, 4, 4)
+    out, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    perm = np.arange(12); perm[4:8] = [6, 4, 7, 5]
+    P = lambda x: x[:, perm]
+    out2, S2 = o.hybrid_layer(P(q), P(k), P(v), P(qp), P(kp), P(vp), a, P(b), s, 4, 1)
+    assert np.max(np.abs(out2 - out[:, perm])) < 1e-12
+    assert np.max(np.abs(S2 - S)) < 1e-12
+
+
+def check_frame_isolation(o):
+    """Changing frame m leaves earlier outputs untouched and the intra branch of
+    every other frame untouched (2.1 item 1, 2.2 frame-level access)."""
+    rng = np.random.default_rng(11)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 16, 2, 4, 4)
+    out, _ = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    k2 = k.copy(); k2[0, 8:12] += 0.5 * rng.standard_normal(k2[0, 8:12].shape)
+    vp2 = vp.copy(); vp2[0, 8:12] += 0.5
+    out2, _ = o.hybrid_layer(q, k2, v, qp, kp, vp2, a, b, s, 4, 1)
+    assert np.max(np.abs(out2[:, :8] - out[:, :8])) == 0.0
+    assert np.max(np.abs(out2[:, 8:12] - out[:, 8:12])) > 1e-6
+    # frame 3 changes only through O_inter (vp of frame 2 moved the state)
+    zero_s = np.zeros_like(s)
+    i1, _ = o.hybrid_layer(q, k, v, 0 * qp, kp, vp, a, b, zero_s, 4, 0)
+    i2, _ = o.hybrid_layer(q, k2, v, 0 * qp, kp, vp2, a, b, zero_s, 4, 0)
+    assert np.max(np.abs(i1[:, 12:] - i2[:, 12:])) == 0.0
+
+
+def check_call_splitting(o):
+    """One F-frame clean call equals F single-frame clean calls."""
+    rng = np.random.default_rng(12)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 2, 15, 2, 4, 5)
+    out, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 5, 1)
+    St = s.copy()
+    for n in range(3):
+        r = slice(5 * n, 5 * n + 5)
+        on, St = o.hybrid_layer(q[:, r], k[:, r], v[:, r], qp[:, r], kp[:, r], vp[:, r],
+                                a[:, n:n + 1], b[:, r], St, 5, 1)
+        assert np.max(np.abs(on - out[:, r])) < 1e-12
+    assert np.max(np.abs(St - S)) < 1e-12
+
+
+def check_denoise_pass_leaves_state(o):
+    """update_state = 0 never writes S; a denoise pass and the clean pass over
+    the same inputs give the same output (2.2 clean-pass updates)."""
+    rng = np.random.default_rng(13)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 4, 2, 4, 4)
+    o0, S0 = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 0)
+    assert np.array_equal(S0, s)
+    o1, S1 = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    assert np.array_equal(o0, o1)
+    assert not np.allclose(S1, s)
+    # with update_state = 0 every frame of a multi-frame call reads the input S
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 8, 1, 4, 4)
+    o2, _ = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 0)
+    for n in range(2):
+        r = slice(4 * n, 4 * n + 4)
+        want = o.intra_frame_attention(q[0, r, 0], k[0, r, 0], v[0, r, 0]) + qp[0, r, 0] @ s[0, 0]
+        assert np.max(np.abs(o2[0, r, 0] - want)) < 1e-13
+
+
+def check_state_chain_matches_layer(o):
+    """state_chain's last state equals the layer's final state, per head."""
+    rng = np.random.default_rng(14)
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, 1, 12, 2, 4, 4)
+    _, S = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, 4, 1)
+    for h in range(2):
+        ch = o.state_chain(kp[0, :, h], vp[0, :, h], a[0, :, h], b[0, :, h], s[0, h], 4)
+        assert len(ch) == 4
+        assert np.max(np.abs(ch[-1] - S[0, h])) < 1e-14
+
+
+ALL_CHECKS = [
+    check_softmax_rows_sum_to_one,
+    check_hand_worked_example,
+    check_single_frame_is_textbook_attention,
+    check_brute_force_tiny,
+    check_alpha1_beta0_keeps_state,
+    check_alpha0_beta0_clears_state,
+    check_beta0_geometric_decay,
+    check_delta_rule_recall,
+    check_affine_form,
+    check_column_separability,
+    check_token_permutation,
+    check_frame_isolation,
+    check_call_splitting,
+    check_denoise_pass_leaves_state,
+    check_state_chain_matches_layer,
+]

@@ -1,0 +1,140 @@
+"""Plant plausible mistakes in a private copy of the oracle (CPU only) and check
+that at least one pin catches each: the pins are only worth something if a
+dropped term, a wrong sign or index, or a transposed operand fails them."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from tests.oracle_pins import ALL_CHECKS
+
+ORACLE_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "oracle", "hybrid_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("oracle_mutant_copy", ORACLE_FILE)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def m_no_transpose(m):
+    def f(state, kp, vp, alpha, beta):
+        return alpha * state + kp @ (beta[:, None] * (vp - kp @ state))
+    m.delta_update = f
+
+
+def m_decayed_residual(m):
+    def f(state, kp, vp, alpha, beta):
+        return alpha * state + kp.T @ (beta[:, None] * (vp - kp @ (alpha * state)))
+    m.delta_update = f
+
+
+def m_sign(m):
+    def f(state, kp, vp, alpha, beta):
+        return alpha * state - kp.T @ (beta[:, None] * (vp - kp @ state))
+    m.delta_update = f
+
+
+def m_drop_alpha(m):
+    def f(state, kp, vp, alpha, beta):
+        return state + kp.T @ (beta[:, None] * (vp - kp @ state))
+    m.delta_update = f
+
+
+def m_drop_beta(m):
+    def f(state, kp, vp, alpha, beta):
+        return alpha * state + kp.T @ (vp - kp @ state)
+    m.delta_update = f
+
+
+def m_drop_residual_term(m):
+    def f(state, kp, vp, alpha, beta):
+        return alpha * state + kp.T @ (beta[:, None] * vp)
+    m.delta_update = f
+
+
+def m_readout_transposed(m):
+    m.inter_frame_readout = lambda qp, state: qp @ state.T
+
+
+def m_softmax_columns(m):
+    def f(z):
+        z = np.asarray(z, dtype=np.float64)
+        e = np.exp(z - z.max(axis=0, keepdims=True))
+        return e / e.sum(axis=0, keepdims=True)
+    m.softmax_rows = f
+
+
+def m_no_scale(m):
+    orig = m.intra_frame_attention
+
+    def f(q, k, v, scale=None):
+        return orig(q, k, v, 1.0 if scale is None else scale)
+    m.intra_frame_attention = f
+
+
+def m_pv_transposed_keys(m):
+    def f(q, k, v, scale=None):
+        s = 1.0 / np.sqrt(q.shape[1]) if scale is None else scale
+        return m.softmax_rows((k @ q.T) * s) @ v
+    m.intra_frame_attention = f
+
+
+def _layer_head_variant(m, read_after_update=False, global_attention=False,
+                        always_update=False, alpha_index_shift=False):
+    def f(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale=None, frames=None):
+        T = q.shape[0]; L = int(frame_len); F = T // L
+        S = np.array(state, dtype=np.float64, copy=True)
+        out = np.full((T, v.shape[1]), np.nan)
+        for n in range(F):
+            r = slice(n * L, (n + 1) * L)
+            kk = slice(0, T) if global_attention else r
+            Snew = S
+            if update_state or always_update:
+                an = float(alpha[min(n + 1, F - 1)] if alpha_index_shift else alpha[n])
+                Snew = m.delta_update(S, kp[r], vp[r], an, beta[r])
+            Sread = Snew if read_after_update else S
+            out[r] = m.intra_frame_attention(q[r], k[kk], v[kk], scale) + m.inter_frame_readout(qp[r], Sread)
+            S = Snew
+        return out, S
+    m.hybrid_layer_head = f
+
+
+MUTANTS = {
+    "no_transpose": m_no_transpose,
+    "decayed_residual": m_decayed_residual,
+    "update_sign": m_sign,
+    "drop_alpha": m_drop_alpha,
+    "drop_beta": m_drop_beta,
+    "drop_residual_term": m_drop_residual_term,
+    "readout_transposed": m_readout_transposed,
+    "softmax_over_columns": m_softmax_columns,
+    "no_softmax_scale": m_no_scale,
+    "scores_transposed": m_pv_transposed_keys,
+    "read_after_update": lambda m: _layer_head_variant(m, read_after_update=True),
+    "attend_across_frames": lambda m: _layer_head_variant(m, global_attention=True),
+    "update_on_denoise": lambda m: _layer_head_variant(m, always_update=True),
+    "alpha_off_by_one": lambda m: _layer_head_variant(m, alpha_index_shift=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    m = fresh_oracle()
+    MUTANTS[name](m)
+    caught = []
+    for check in ALL_CHECKS:
+        try:
+            check(m)
+        except Exception as e:  # noqa: BLE001 - any failure (assert or shape error) is a catch
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes():
+    m = fresh_oracle()
+    for check in ALL_CHECKS:
+        check(m)
