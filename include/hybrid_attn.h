@@ -1,0 +1,142 @@
+/*
+ * hybrid_attn.h - C ABI of the MI355X (gfx950) hybrid attention layer.
+ *
+ * The layer is the ARL2 hybrid attention of an autoregressive video diffusion
+ * transformer ("Attend Locally, Remember Linearly", arXiv 2605.16579,
+ * section 2.1 "hybrid attention decomposition" and section 2.2 "state
+ * management"). Per stream b and head h, frame N (tokens [N*L, (N+1)*L)):
+ *
+ *   O_N   = softmax(Q_N K_N^T * s) V_N  +  Q'_N S_{N-1}           (2.1)
+ *   S_N   = alpha_N S_{N-1} + K'_N^T diag(beta_N) (V'_N - K'_N S_{N-1})  (2.1)
+ *
+ * The softmax runs among the L tokens of the frame only, in both directions
+ * (2.1 item 1); the two branches are summed; every token of frame N reads the
+ * same pre-update state S_{N-1} and the state is written only after the whole
+ * frame, and only on the clean pass (2.2).
+ *
+ * Layouts (all row-major, last index contiguous):
+ *   q, k, v, qp, kp, vp, out : [B, T, H, d]   T = F * frame_len
+ *   alpha                    : [B, F, H]      fp32
+ *   beta                     : [B, T, H]      fp32
+ *   state                    : [B, H, d, d]   fp32, state[b][h][dk][dv]
+ * q..vp and out are bf16 (HA_BF16) or fp32 (HA_FP32); state is always fp32.
+ *
+ * Ownership: every pointer is device memory owned by the caller (for example
+ * allocated through PyTorch). The library allocates nothing and keeps no
+ * state between calls; scratch space is the caller's workspace argument.
+ *
+ * Execution: calls are asynchronous on the given HIP stream (a hipStream_t
+ * passed as void*; NULL is the default stream). A call returns after
+ * enqueueing its kernels. Argument errors are returned before any device
+ * work is enqueued and leave every buffer untouched; a failed launch returns
+ * HA_ERR_DEVICE; a fault inside a kernel surfaces at the caller's next
+ * synchronisation. Calls are reentrant: there is no global mutable state.
+ * Two calls that share a state or workspace buffer must be ordered by the
+ * caller (for example by issuing them on one stream).
+ */
+#ifndef HYBRID_ATTN_H
+#define HYBRID_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HA_BF16 = 0, /* q..vp and out are bfloat16 */
+  HA_FP32 = 1  /* q..vp and out are float32 */
+} ha_dtype;
+
+typedef enum {
+  HA_OK = 0,
+  HA_ERR_NULL = 1,        /* a required pointer is NULL */
+  HA_ERR_SHAPE = 2,       /* a size <= 0, T % frame_len != 0, or a size too large to index */
+  HA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or an unknown dtype */
+  HA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned (alpha, beta: 4-byte) */
+  HA_ERR_WORKSPACE = 5,   /* workspace is NULL or smaller than the size the query returns */
+  HA_ERR_DEVICE = 6,      /* a kernel launch failed */
+  HA_ERR_ALIAS = 7        /* out overlaps an input, the state, or the workspace */
+} ha_status;
+
+/*
+ * Bytes of workspace hybrid_attn_forward needs for these sizes: 0 when
+ * update_state is 0; otherwise the per-frame state increments (d x 2d fp32 per
+ * stream, head and frame) plus, when T / frame_len > 1, the per-frame
+ * pre-update states S_{N-1} (d x d fp32 each). Returns 0 for invalid sizes.
+ */
+size_t hybrid_attn_workspace_bytes(int B, int H, int T, int frame_len, int d,
+                                   int update_state);
+
+/*
+ * The whole layer call (ARL2 2.1 and 2.2).
+ *   q, k, v      intra-frame branch inputs (the frozen softmax projections)
+ *   qp, kp, vp   inter-frame branch inputs Q', K', V' (after the feature maps)
+ *   alpha        forget gate per (stream, frame, head), read if update_state
+ *   beta         step size per (stream, token, head), read if update_state
+ *   state        S in/out: frame 0 reads it; with update_state != 0 it is
+ *                overwritten with S_F after the last frame, otherwise it is
+ *                left bitwise unchanged and every frame reads it
+ *   out          O, written in full
+ *   workspace    caller scratch of at least hybrid_attn_workspace_bytes(...)
+ *   softmax_scale  s; a value <= 0 selects 1/sqrt(d)
+ * When update_state is 0, kp, vp, alpha, beta and workspace may be NULL.
+ * out must not overlap any input, the state or the workspace (HA_ERR_ALIAS).
+ */
+ha_status hybrid_attn_forward(const void* q, const void* k, const void* v,
+                              const void* qp, const void* kp, const void* vp,
+                              const float* alpha, const float* beta,
+                              float* state, void* out,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int H, int T, int d, int frame_len,
+                              ha_dtype dtype, int update_state,
+                              float softmax_scale, void* stream);
+
+/*
+ * The read side alone (ARL2 2.1 intra-frame branch plus the Q'S readout,
+ * 2.2 frame-level access): out = softmax-within-frame(Q K^T s) V + Q' S_n for
+ * every frame n, where S_n is the fp32 d x d matrix at
+ *   states + b*state_stride_bh + n*state_stride_frame   (in floats).
+ * With state_stride_frame = 0 every frame reads the same state (a denoising
+ * pass). Nothing but out is written.
+ */
+ha_status hybrid_attn_intra_readout(const void* q, const void* k,
+                                    const void* v, const void* qp,
+                                    const float* states,
+                                    long long state_stride_bh,
+                                    long long state_stride_frame, void* out,
+                                    int B, int H, int T, int d, int frame_len,
+                                    ha_dtype dtype, float softmax_scale,
+                                    void* stream);
+
+/*
+ * Bytes of workspace hybrid_attn_state_update needs: the per-frame state
+ * increments, B*H*F*d*2d fp32. Returns 0 for invalid sizes.
+ */
+size_t hybrid_attn_state_workspace_bytes(int B, int H, int T, int frame_len,
+                                         int d);
+
+/*
+ * The write side alone (ARL2 2.1 update rule, applied once per clean frame as
+ * 2.2 prescribes): state <- S_F after frames 0..F-1 of kp, vp, alpha, beta.
+ * If snapshots is not NULL it receives S_{n-1} for every frame n, laid out
+ * [B, H, F, d, d] fp32 (snapshot n of frame 0 is the input state).
+ */
+ha_status hybrid_attn_state_update(const void* kp, const void* vp,
+                                   const float* alpha, const float* beta,
+                                   float* state, float* snapshots,
+                                   void* workspace, size_t workspace_bytes,
+                                   int B, int H, int T, int d, int frame_len,
+                                   ha_dtype dtype, void* stream);
+
+/* A static, human-readable description of a status code. */
+const char* hybrid_attn_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int hybrid_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYBRID_ATTN_H */

@@ -1,0 +1,178 @@
+"""Thin ctypes binding of libhybrid_attn.so (the C ABI in include/hybrid_attn.h).
+
+Only argument marshalling lives here: checks of device, dtype, shape and
+contiguity, allocation of the output and the workspace through PyTorch, and
+the current HIP stream. Every step of the layer runs in the HIP kernels.
+There is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HA_BF16, HA_FP32 = 0, 1
+STATUS = {0: "HA_OK", 1: "HA_ERR_NULL", 2: "HA_ERR_SHAPE", 3: "HA_ERR_UNSUPPORTED",
+          4: "HA_ERR_ALIGN", 5: "HA_ERR_WORKSPACE", 6: "HA_ERR_DEVICE", 7: "HA_ERR_ALIAS"}
+EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_intra_readout",
+           "hybrid_attn_state_update", "hybrid_attn_state_workspace_bytes",
+           "hybrid_attn_status_string", "hybrid_attn_version")
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_attn.so")
+_lib = None
+
+
+class HybridAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library once; raise if it is missing (no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m video_dit_hybrid_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, sz, f, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_longlong
+    L.hybrid_attn_forward.argtypes = [vp] * 10 + [vp, sz, i, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_forward.restype = i
+    L.hybrid_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.hybrid_attn_workspace_bytes.restype = sz
+    L.hybrid_attn_intra_readout.argtypes = [vp, vp, vp, vp, vp, ll, ll, vp, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_intra_readout.restype = i
+    L.hybrid_attn_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, vp]
+    L.hybrid_attn_state_update.restype = i
+    L.hybrid_attn_state_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.hybrid_attn_state_workspace_bytes.restype = sz
+    L.hybrid_attn_status_string.argtypes = [i]
+    L.hybrid_attn_status_string.restype = ctypes.c_char_p
+    L.hybrid_attn_version.argtypes = []
+    L.hybrid_attn_version.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().hybrid_attn_status_string(int(status)).decode()
+
+
+def workspace_bytes(B, H, T, frame_len, d, update_state) -> int:
+    return int(lib().hybrid_attn_workspace_bytes(B, H, T, frame_len, d, int(bool(update_state))))
+
+
+def state_workspace_bytes(B, H, T, frame_len, d) -> int:
+    return int(lib().hybrid_attn_state_workspace_bytes(B, H, T, frame_len, d))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return HA_BF16
+    if t.dtype == torch.float32:
+        return HA_FP32
+    raise TypeError(f"q..v' must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(name, t, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def hybrid_attn_forward(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state,
+                        softmax_scale: float = 0.0, out=None, workspace=None):
+    """The layer call: returns out [B,T,H,d]; with update_state the fp32 state
+    [B,H,d,d] is advanced in place to S_F, otherwise it is left unchanged.
+    Layouts as in include/hybrid_attn.h. Asynchronous on the current stream."""
+    torch = _torch()
+    if q.device.type != "cuda":
+        raise ValueError("hybrid_attn_forward runs on a GPU; tensors must be on a cuda device")
+    B, T, H, d = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    F = T // frame_len if frame_len > 0 and T % frame_len == 0 else -1
+    if F <= 0:
+        raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
+    for name, t in (("k", k), ("v", v), ("qp", qp)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    _check("state", state, (B, H, d, d), torch.float32, dev)
+    if update_state:
+        for name, t in (("kp", kp), ("vp", vp)):
+            _check(name, t, (B, T, H, d), dt, dev)
+        _check("alpha", alpha, (B, F, H), torch.float32, dev)
+        _check("beta", beta, (B, T, H), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, T, H, d), dt, dev)
+    need = workspace_bytes(B, H, T, frame_len, d, update_state)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().hybrid_attn_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(qp), _ptr(kp if update_state else None),
+        _ptr(vp if update_state else None), _ptr(alpha if update_state else None),
+        _ptr(beta if update_state else None), _ptr(state), _ptr(out),
+        _ptr(workspace), ws_bytes, B, H, T, d, frame_len, code, int(bool(update_state)),
+        float(softmax_scale), _stream(dev))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_forward")
+    return out
+
+
+def hybrid_attn_intra_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame,
+                              frame_len, softmax_scale: float = 0.0, out=None):
+    """Read side only: out = softmax-within-frame(QK^T s)V + Q' S_n, with S_n the
+    fp32 d x d block at states + b*stride_bh + n*stride_frame (in floats)."""
+    B, T, H, d = q.shape
+    code = _dtype_code(q)
+    if out is None:
+        out = _torch().empty_like(q)
+    st = lib().hybrid_attn_intra_readout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(qp), _ptr(states), int(state_stride_bh),
+        int(state_stride_frame), _ptr(out), B, H, T, d, frame_len, code, float(softmax_scale),
+        _stream(q.device))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_intra_readout")
+    return out
+
+
+def hybrid_attn_state_update(kp, vp, alpha, beta, state, frame_len, snapshots=None, workspace=None):
+    """Write side only: advance the fp32 state in place over the frames of
+    kp, vp, alpha, beta; optionally write S_{n-1} of every frame to snapshots
+    [B,H,F,d,d]."""
+    torch = _torch()
+    B, T, H, d = kp.shape
+    code = _dtype_code(kp)
+    need = state_workspace_bytes(B, H, T, frame_len, d)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=kp.device)
+    st = lib().hybrid_attn_state_update(
+        _ptr(kp), _ptr(vp), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(snapshots),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, d, frame_len,
+        code, _stream(kp.device))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_state_update")
+    return state

@@ -1,0 +1,70 @@
+// Device-side helpers shared by the gfx950 kernels of the hybrid attention layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ha {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] * B[16x32], fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) .. +8) and B[8*(l/32) .. +8)[l%32]; it gets
+// back C[8*(r/4) + 4*(l/32) + r%4][l%32] in element r.
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> one dword of two bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element e (0..7) of eight packed bf16, as its 16-bit pattern.
+__device__ __forceinline__ uint32_t bf16_elem(const u32x4& v, int e) {
+  uint32_t w = v[e >> 1];
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// max over the two lanes l and l^32 that hold the same MFMA output column.
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ u32x4 ld_global_16B(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void st_global_8B(void* p, u32x2 v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+
+// Work-group index -> work item, so that consecutive work items land on the
+// same XCD (work-groups are dealt to the 8 XCDs round-robin, and each XCD has
+// its own L2). Requires gridDim.x % 8 == 0; items >= n_items are padding.
+__device__ __forceinline__ int xcd_major_item(int n_groups) {
+  const int g = blockIdx.x;
+  const int per_xcd = n_groups >> 3;
+  return (g & 7) * per_xcd + (g >> 3);
+}
+
+}  // namespace ha

@@ -1,0 +1,196 @@
+// C ABI of the hybrid attention layer: argument validation, workspace layout
+// and launch order. The kernels live in attn_bf16.hip, state_bf16.hip,
+// state_scan.hip and fp32_path.hip.
+//
+// Launch order of a call (ARL2 section 2.2: every token of frame N reads
+// S_{N-1}; the state is written once per clean frame, after the frame):
+//   update_state = 0      : readout kernel on `state` for every frame.
+//   update_state = 1, F=1 : readout on `state`, then gram, then the scan
+//                           writes S_1 into `state` (same stream, so the
+//                           readout has read S_0 before it is overwritten).
+//   update_state = 1, F>1 : gram, scan (writes S_{n-1} snapshots to the
+//                           workspace and S_F to `state`), then the readout
+//                           on the snapshots.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/hybrid_attn.h"
+#include "ha_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Largest element count the kernels index with 32-bit work decomposition.
+constexpr long long kMaxItems = 0x7fffffffLL;
+
+ha_status check_shape(int B, int H, int T, int d, int L, int dtype, ha::Shape* s) {
+  if (B <= 0 || H <= 0 || T <= 0 || L <= 0 || d <= 0) return HA_ERR_SHAPE;
+  if (T % L != 0) return HA_ERR_SHAPE;
+  if (d != 64 && d != 128) return HA_ERR_UNSUPPORTED;
+  if (dtype != HA_BF16 && dtype != HA_FP32) return HA_ERR_UNSUPPORTED;
+  // work items of the widest launch (fp32 readout: 64 queries per item)
+  const long long items = (long long)B * H * (T / L) * ((L + 63) / 64);
+  if (items > kMaxItems) return HA_ERR_SHAPE;
+  if ((long long)B * H * (T / L) * 2 > kMaxItems) return HA_ERR_SHAPE;
+  *s = ha::Shape{B, H, T, d, L, T / L};
+  return HA_OK;
+}
+
+size_t tensor_bytes(const ha::Shape& s, int dtype) {
+  return (size_t)s.B * s.T * s.H * (size_t)s.d * (dtype == HA_BF16 ? 2 : 4);
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / sqrtf((float)d); }
+
+ha_status launched(hipError_t e) { return e == hipSuccess ? HA_OK : HA_ERR_DEVICE; }
+
+ha_status run_readout(const void* q, const void* k, const void* v, const void* qp,
+                      const float* states, long long sbh, long long sfr, void* out,
+                      const ha::Shape& s, int dtype, float scale, hipStream_t st) {
+  if (dtype == HA_BF16)
+    return launched(ha::launch_attn_bf16(q, k, v, qp, states, sbh, sfr, out, s, scale, st));
+  return launched(ha::launch_attn_fp32(q, k, v, qp, states, sbh, sfr, out, s, scale, st));
+}
+
+ha_status run_update(const void* kp, const void* vp, const float* alpha, const float* beta,
+                     float* state, float* snaps, float* gram, const ha::Shape& s, int dtype,
+                     hipStream_t st) {
+  hipError_t e = dtype == HA_BF16 ? ha::launch_gram_bf16(kp, vp, beta, gram, s, st)
+                                  : ha::launch_gram_fp32(kp, vp, beta, gram, s, st);
+  if (e != hipSuccess) return HA_ERR_DEVICE;
+  return launched(ha::launch_state_scan(gram, alpha, state, snaps, s, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hybrid_attn_version(void) { return 100; }
+
+const char* hybrid_attn_status_string(int status) {
+  switch (status) {
+    case HA_OK: return "ok";
+    case HA_ERR_NULL: return "a required pointer is NULL";
+    case HA_ERR_SHAPE: return "invalid sizes (non-positive, T not a multiple of frame_len, or too large)";
+    case HA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128) or dtype";
+    case HA_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes; alpha and beta 4 bytes)";
+    case HA_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case HA_ERR_DEVICE: return "a kernel launch failed";
+    case HA_ERR_ALIAS: return "out overlaps an input, the state or the workspace";
+    default: return "unknown status";
+  }
+}
+
+size_t hybrid_attn_state_workspace_bytes(int B, int H, int T, int frame_len, int d) {
+  ha::Shape s;
+  if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK) return 0;
+  return align_up(ha::gram_bytes(s));
+}
+
+size_t hybrid_attn_workspace_bytes(int B, int H, int T, int frame_len, int d, int update_state) {
+  ha::Shape s;
+  if (!update_state) return 0;
+  if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK) return 0;
+  size_t n = align_up(ha::gram_bytes(s));
+  if (s.F > 1) n += align_up(ha::snapshot_bytes(s));
+  return n;
+}
+
+ha_status hybrid_attn_intra_readout(const void* q, const void* k, const void* v, const void* qp,
+                                    const float* states, long long state_stride_bh,
+                                    long long state_stride_frame, void* out, int B, int H, int T,
+                                    int d, int frame_len, ha_dtype dtype, float softmax_scale,
+                                    void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (!q || !k || !v || !qp || !states || !out) return HA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qp, 16) ||
+      !aligned(states, 16) || !aligned(out, 16))
+    return HA_ERR_ALIGN;
+  if (state_stride_bh < 0 || state_stride_frame < 0 || state_stride_bh % 4 || state_stride_frame % 4)
+    return HA_ERR_ALIGN;
+  const size_t tb = tensor_bytes(s, dtype);
+  const size_t sb = (size_t)((B * (long long)H - 1) * state_stride_bh +
+                             (s.F - 1) * state_stride_frame + (long long)d * d) * sizeof(float);
+  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
+      overlap(out, tb, qp, tb) || overlap(out, tb, states, sb))
+    return HA_ERR_ALIAS;
+  return run_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame, out, s, dtype,
+                     resolve_scale(softmax_scale, d), (hipStream_t)stream);
+}
+
+ha_status hybrid_attn_state_update(const void* kp, const void* vp, const float* alpha,
+                                   const float* beta, float* state, float* snapshots,
+                                   void* workspace, size_t workspace_bytes, int B, int H, int T,
+                                   int d, int frame_len, ha_dtype dtype, void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (!kp || !vp || !alpha || !beta || !state || !workspace) return HA_ERR_NULL;
+  if (!aligned(kp, 16) || !aligned(vp, 16) || !aligned(state, 16) || !aligned(workspace, 16) ||
+      !aligned(alpha, 4) || !aligned(beta, 4) || (snapshots && !aligned(snapshots, 16)))
+    return HA_ERR_ALIGN;
+  if (workspace_bytes < hybrid_attn_state_workspace_bytes(B, H, T, frame_len, d))
+    return HA_ERR_WORKSPACE;
+  return run_update(kp, vp, alpha, beta, state, snapshots, (float*)workspace, s, dtype,
+                    (hipStream_t)stream);
+}
+
+ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const void* qp,
+                              const void* kp, const void* vp, const float* alpha,
+                              const float* beta, float* state, void* out, void* workspace,
+                              size_t workspace_bytes, int B, int H, int T, int d, int frame_len,
+                              ha_dtype dtype, int update_state, float softmax_scale,
+                              void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (!q || !k || !v || !qp || !state || !out) return HA_ERR_NULL;
+  if (update_state && (!kp || !vp || !alpha || !beta)) return HA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qp, 16) ||
+      !aligned(state, 16) || !aligned(out, 16))
+    return HA_ERR_ALIGN;
+  if (update_state && (!aligned(kp, 16) || !aligned(vp, 16) || !aligned(alpha, 4) ||
+                       !aligned(beta, 4) || !aligned(workspace, 16)))
+    return HA_ERR_ALIGN;
+  const size_t need = hybrid_attn_workspace_bytes(B, H, T, frame_len, d, update_state);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return HA_ERR_WORKSPACE;
+
+  const size_t tb = tensor_bytes(s, dtype);
+  const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
+  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
+      overlap(out, tb, qp, tb) || overlap(out, tb, state, stb) ||
+      (update_state && (overlap(out, tb, kp, tb) || overlap(out, tb, vp, tb) ||
+                        overlap(out, tb, workspace, need))))
+    return HA_ERR_ALIAS;
+
+  const float scale = resolve_scale(softmax_scale, d);
+  hipStream_t st = (hipStream_t)stream;
+  const long long dd = (long long)d * d;
+  if (!update_state)
+    return run_readout(q, k, v, qp, state, dd, 0, out, s, dtype, scale, st);
+
+  float* gram = (float*)workspace;
+  if (s.F == 1) {
+    r = run_readout(q, k, v, qp, state, dd, 0, out, s, dtype, scale, st);
+    if (r != HA_OK) return r;
+    return run_update(kp, vp, alpha, beta, state, nullptr, gram, s, dtype, st);
+  }
+  float* snaps = (float*)((char*)workspace + align_up(ha::gram_bytes(s)));
+  r = run_update(kp, vp, alpha, beta, state, snaps, gram, s, dtype, st);
+  if (r != HA_OK) return r;
+  return run_readout(q, k, v, qp, snaps, (long long)s.F * dd, dd, out, s, dtype, scale, st);
+}
+
+}  // extern "C"

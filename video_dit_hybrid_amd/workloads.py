@@ -192,3 +192,22 @@ def call_schedule(w: Workload):
             sched.append((f, w.frames_per_call, p, False))
         sched.append((f, w.frames_per_call, w.denoise_passes, True))
     return sched
+
+
+def as_torch(x: np.ndarray, dtype: str, device="cuda"):
+    """Storage array -> torch tensor on device, same bytes (bf16 bits are viewed, not converted)."""
+    import torch
+    if dtype == "bf16" and x.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device)
+
+
+def from_torch(t, dtype: str) -> np.ndarray:
+    """Device tensor -> storage array (bf16 as uint16 bits, fp32 as float32)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
