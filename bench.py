@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "tiny"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--kernel", choices=["attn", "update", "copy"], default=None,
+                    help="launch only one phase (readout-only attention, or the state update) "
+                         "steps times, for profilers; prints its average time")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -134,6 +137,48 @@ def main():
     state = torch.from_numpy(s0.copy()).to(dev)
     out = torch.empty_like(t["q"])
     ws = torch.empty(max(1, api.workspace_bytes(w.B, w.H, w.T, w.L, w.d, 1)), dtype=torch.uint8, device=dev)
+
+    if args.kernel == "copy":
+        # calibration for memory counters: a plain 256 MiB device-to-device copy
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        print(json.dumps({"kernel": "copy", "bytes_read": src.numel() * 4, "bytes_written": src.numel() * 4,
+                          "avg_ms": ms, "GB_s": 2 * src.numel() * 4 / ms / 1e6}), flush=True)
+        return
+    if args.kernel:
+        snaps = torch.empty((w.B, w.H, w.frames, w.d, w.d), dtype=torch.float32, device=dev)
+        api.hybrid_attn_state_update(t["kp"], t["vp"], t["alpha"], t["beta"], state, w.L, snapshots=snaps)
+        gws = torch.empty(max(1, api.state_workspace_bytes(w.B, w.H, w.T, w.L, w.d)), dtype=torch.uint8, device=dev)
+
+        def one():
+            if args.kernel == "attn":
+                api.hybrid_attn_intra_readout(t["q"], t["k"], t["v"], t["qp"], snaps, w.frames * w.d * w.d,
+                                              w.d * w.d, w.L, out=out)
+            else:
+                api.hybrid_attn_state_update(t["kp"], t["vp"], t["alpha"], t["beta"], state, w.L,
+                                             snapshots=snaps, workspace=gws)
+        for _ in range(args.warmup):
+            one()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            one()
+        ev1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": args.kernel, "workload": w.name, "launches": args.steps,
+                          "avg_ms": ev0.elapsed_time(ev1) / args.steps}), flush=True)
+        return
 
     def step():
         api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], t["kp"], t["vp"], t["alpha"],

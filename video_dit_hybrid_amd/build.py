@@ -26,6 +26,7 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

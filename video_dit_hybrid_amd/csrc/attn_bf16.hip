@@ -8,26 +8,39 @@
 // where the softmax runs over the keys of frame n only.
 //
 // Work decomposition: one work-group (4 waves, 256 threads) owns 128 queries
-// of one (b, h, frame); each wave owns 32 queries. Key/value tiles of 64 keys
-// are staged in LDS (double buffered) and shared by the 4 waves.
+// of one (b, h, frame); each wave owns 32 queries. Key and value tiles of 64
+// keys are copied global -> LDS by buffer loads that write LDS directly
+// (no VGPR staging), two tiles in flight, and shared by the 4 waves. Rows past
+// the end of the frame are outside the buffer descriptor's range and arrive as
+// zeros, so no load is predicated.
 //
-// Orientation: the wave computes S^T = K Q^T (keys x queries) so that every
-// lane holds 16 scores of ONE query (column l%32) per 32x32 block. The row
-// max and row sum are then in-lane reductions plus one permlane32 swap, and
-// the output accumulator O^T (dv x queries) of a lane also belongs to one
-// query, so the softmax rescale is a per-lane scalar.
+// Orientation: a wave computes S^T = K Q^T (keys x queries) so that every lane
+// holds 16 scores of ONE query (column l%32) per 32x32 block. Row max and row
+// sum are in-lane reductions plus one permlane32 swap, and the output
+// accumulator O^T (dv x queries) of a lane also belongs to one query, so the
+// softmax rescale is a per-lane scalar.
 //
 // Key permutation: MFMA row i of the S^T block reads physical key pi(i), pi
-// swapping bits 2 and 3 of i. With it, lane half hh holds physical keys
-// [16*(r/8) + 8*hh + r%8] in accumulator element r, i.e. eight CONSECUTIVE keys
-// per k-step of the P V product, so P feeds the B operand of O^T += V^T P^T
-// straight from registers and V^T is read from LDS as one 16-byte chunk.
+// swapping bits 2 and 3 of i. Then lane half hh holds the eight CONSECUTIVE
+// keys 16*(r/8) + 8*hh + r%8 in accumulator elements r, which is exactly the
+// B-operand layout of O^T += V^T P^T, so P feeds the next MFMA from registers.
+// V stays row-major in LDS; its A operand (8 consecutive keys of one dv column
+// per lane) comes from two ds_read_b64_tr_b16, which hand each lane of a
+// 16-lane group one column of a 4 x 16 block that the group reads row-wise.
 //
+// Per key tile: S^T = K Q^T (16 MFMAs), online softmax on the VALU, then
+// O^T += V^T P^T (16 MFMAs); the next tile's K and V are already in flight to
+// the other LDS buffer. Inside each MFMA phase the LDS operand of MFMA i+4 is
+// read while MFMA i issues, so LDS latency is hidden within the wave; two waves
+// per SIMD (two work-groups per CU) overlap one wave's softmax with the other's
+// MFMA phases.
 // Online softmax in the exp2 domain with the scale folded into one FMA; the
-// running max is only moved when a tile's max exceeds it by more than 8
-// (log2 units), so exp2 arguments stay <= 8 and rescales of the accumulator
-// are rare after the first tiles (the result is exact either way: any
-// reference point common to numerator and denominator cancels).
+// running max only moves when a tile's max exceeds it by more than 8 (log2
+// units), so exp2 arguments stay <= 8 and accumulator rescales are rare. The
+// result does not depend on that choice: a reference point common to the
+// numerator and the denominator cancels.
+#include <type_traits>
+
 #include "ha_device.h"
 #include "ha_launch.h"
 
@@ -40,47 +53,87 @@ constexpr int NW = 4;           // waves per work-group
 constexpr int QPB = QPW * NW;   // queries per work-group
 constexpr int NT = NW * kWave;  // threads per work-group
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
 
 template <int D>
 struct Cfg {
   static constexpr int NCH = D / 8;          // 16-byte chunks in a row of D bf16
-  static constexpr int K_TILE = KT * D * 2;  // bytes of the K tile
-  static constexpr int V_TILE = D * KT * 2;  // bytes of the V^T tile
-  static constexpr int BUF = K_TILE + V_TILE;
-  static constexpr int SMEM = 2 * BUF;       // double buffer; also holds S^T (D*D*2)
+  static constexpr int TILE = KT * D * 2;    // bytes of one K or V tile
+  static constexpr int SMEM = 4 * TILE;      // K[2] then V[2]; also holds S (D*D*2)
   static constexpr int KSTEPS = D / 16;      // MFMA k-steps over d
   static constexpr int DB = D / 32;          // 32-row blocks of O^T
-  static constexpr int K_LD = KT * NCH / NT; // K chunks loaded per thread per tile
-  static constexpr int KPT = NCH / 4;        // keys per thread in the V transpose
-  static constexpr int KQN = NT / NCH;       // key groups in the V transpose
-  static_assert(SMEM >= D * D * 2, "S^T must fit in the tile buffers");
-  static_assert(KQN * KPT == KT, "V transpose must cover the tile");
+  static constexpr int NLD = TILE / 1024 / NW;  // 1 KB direct-to-LDS loads per wave per tile
+  static_assert(SMEM >= D * D * 2, "S must fit in the tile buffers");
+  static_assert(NLD >= 1, "tile too small for the load split");
 };
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t lds_ptr(void* p) { return (lds_ptr_t)p; }
 
 __device__ __forceinline__ int pi32(int i) {  // swap bits 2 and 3
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// XOR swizzles of 16-byte chunks: rows read by 16 consecutive lanes land on
-// 16 distinct chunk slots (and 8 consecutive lanes on 8), so ds_read_b128 of
-// a column of chunks is free of bank conflicts for 128- and 256-byte banks.
+// K tile [KT][D]: 32 lanes read one 16-byte chunk column of rows pi(0..31);
+// the XOR puts 16 consecutive lanes on 16 distinct chunk slots.
 template <int NCH>
-__device__ __forceinline__ int swz_row(int i) {
+__device__ __forceinline__ int k_swz(int row) {
+  const int i = pi32(row & 31);
   if constexpr (NCH >= 16) return i & 15;
   else return (i & 7) ^ ((i >> 3) & 1);
 }
+// V tile [KT][D] (and S [D][D]) read by ds_read_b64_tr_b16: 32 lanes (one
+// 256-byte LDS cycle) read 4 consecutive rows x 64 bytes, i.e. four aligned
+// 16-byte chunks per row; XOR-ing the chunk index with 4*(row%4) puts the four
+// rows on disjoint 64-byte bank groups (measured conflict-free on gfx950).
+template <int NCH>
+__device__ __forceinline__ int v_swz(int row) {
+  if constexpr (NCH >= 16) return 4 * (row & 3) + 2 * ((row >> 3) & 1);
+  else return 2 * (row & 3);
+}
 
-template <int D>
-__device__ __forceinline__ int k_off(int row, int ch) {  // K tile [KT][D]
-  return row * (D * 2) + ((ch ^ swz_row<D / 8>(pi32(row & 31))) << 4);
+__device__ __forceinline__ u32x2 ds_read_tr16(const unsigned char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(lds_ptr((void*)p)));
+  return __builtin_bit_cast(u32x2, r);
 }
-__device__ __forceinline__ int vt_off(int dv, int kc) {  // V^T tile [D][KT]
-  return dv * (KT * 2) + ((kc ^ swz_row<8>(dv)) << 4);
+
+// 16 bytes per lane, global (buffer) -> LDS without passing through VGPRs:
+// lane l writes LDS bytes [lds + 16*l, lds + 16*l + 16). The range check of the
+// descriptor covers voff + soff; out-of-range lanes write zeros. The builtin is
+// only compiled in the device pass: clang's host pass drops the host handle of
+// a kernel template whose body names it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 16, voff, soff, 0, 0);
+#endif
 }
-template <int D>
-__device__ __forceinline__ int st_off(int dv, int ch) {  // S^T [D][D]
-  return dv * (D * 2) + ((ch ^ swz_row<D / 8>(dv)) << 4);
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+
+// Scheduling groups for the preceding code of the same basic block (mask: 0x8
+// MFMA, 0x100 LDS read, 0x402 VALU incl. transcendental): PF*R reads first,
+// then per MFMA R reads (while reads remain) and V VALU instructions, so the
+// MFMA pipe, the LDS and the VALU work of one wave interleave.
+template <int N, int PF, int R, int V>
+__device__ __forceinline__ void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PF * R, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    if (V > 0) __builtin_amdgcn_sched_group_barrier(0x402, V, 0);
+  }
+}
+
+template <int P_, bool NEXT_, bool TAIL_, bool LOADK_>
+struct StepFlags {
+  static constexpr int P = P_;
+  static constexpr bool NEXT = NEXT_, TAIL = TAIL_, LOADK = LOADK_;
+};
 
 template <int D>
 __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
@@ -90,7 +143,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     uint16_t* __restrict__ out, int H, int T, int L, int F, int qtiles, int n_items,
     float c2 /* softmax scale * log2(e) */) {
   using C = Cfg<D>;
+  constexpr int NCH = C::NCH;
   __shared__ __align__(16) unsigned char smem[C::SMEM];
+  unsigned char* const kbuf = smem;                 // two K tiles
+  unsigned char* const vbuf = smem + 2 * C::TILE;   // two V tiles
 
   const int item = xcd_major_item(gridDim.x);
   if (item >= n_items) return;
@@ -101,183 +157,286 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   const int b = hf / (H * F);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int lr = lane & 31, hh = lane >> 5;
-  const long long rs = (long long)H * D;  // elements between consecutive tokens
-  const long long fbase = ((long long)b * T + (long long)n * L) * rs + (long long)h * D;
+  const uint32_t rsb = (uint32_t)H * D * 2;  // bytes between consecutive tokens
+  const long long fbase = ((long long)b * T + (long long)n * L) * ((long long)H * D) + (long long)h * D;
+  // bytes of this (b, h, frame) slab as one buffer: tokens >= L read as zero
+  const int span = (int)((uint32_t)(L - 1) * rsb + D * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + fbase), 0, span, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + fbase), 0, span, kRsrcWord3);
 
   const int q0 = qt * QPB + wave * QPW;
   const bool wave_active = q0 < L;
   const int my_q = q0 + lr;
-  const bool q_valid = my_q < L;
+
+  // ---- direct-to-LDS tile loads. Load i of wave w fills the 1 KB LDS segment
+  // seg = i*NW + w of the tile (lane l: 16-byte slot seg*64 + l), i.e. rows
+  // 16*i*(NCH/16)... of the tile. Segments of one wave are 16 rows apart for
+  // D = 128 (8 rows apart for D = 64), which leaves both swizzles unchanged,
+  // so the per-lane byte offset of load i is the offset of load 0 plus a
+  // uniform step.
+  constexpr int ROWS_PER_SEG = 64 / NCH;
+  constexpr int SEG_ROW_STEP = NW * ROWS_PER_SEG;  // rows between a wave's segments
+  static_assert(SEG_ROW_STEP % 8 == 0 || NCH < 16, "segment step must keep the swizzle");
+  uint32_t koff0, voff0;
+  {
+    const int row = wave * ROWS_PER_SEG + lane / NCH, pc = lane % NCH;
+    koff0 = row * rsb + ((pc ^ k_swz<NCH>(row)) << 4);
+    voff0 = row * rsb + ((pc ^ v_swz<NCH>(row)) << 4);
+  }
+  auto issue_k = [&](int j, int buf) {
+    const uint32_t toff = (uint32_t)j * KT * rsb;
+#pragma unroll
+    for (int i = 0; i < C::NLD; ++i)
+      dma16(rk, kbuf + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
+  };
+  auto issue_v = [&](int j, int buf) {
+    const uint32_t toff = (uint32_t)j * KT * rsb;
+#pragma unroll
+    for (int i = 0; i < C::NLD; ++i)
+      dma16(rv, vbuf + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
+  };
+
+  // ---- per-lane LDS read offsets
+  // K (A operand of S^T = K Q^T): row kb*32 + pi(lr), chunk 2*ks + hh, stored at
+  // chunk (2*ks + hh) ^ sw; as 2*ks + hh == 2*ks ^ hh that byte offset is
+  // kaddr ^ (ks << 5) with one per-lane base.
+  const int krow = pi32(lr);
+  const int kaddr = krow * (D * 2) + ((hh ^ k_swz<NCH>(krow)) << 4);
+  // V / S (A operand through transposed reads): a 16-lane group g = lane/16 reads
+  // rows rb + 8*hh + (i/4) (+4 for the second read), columns 16*(g%2) + 4*(i%4)
+  const int gi = lane & 15, g = lane >> 4;
+  const int vrow = 8 * hh + (gi >> 2);
+  const int vsw = v_swz<NCH>(vrow);
+  const int vcol = 16 * (g & 1) + 4 * (gi & 3);  // + 32*db
+  auto v_off = [&](int row_add, int db) {  // row_add multiple of 4 and of no bit-3 effect on the swizzle
+    const int col = vcol + 32 * db;
+    return (vrow + row_add) * (D * 2) + (((col >> 3) ^ vsw) << 4) + (col & 7) * 2;
+  };
 
   u32x4 qf[C::KSTEPS];
+  {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + fbase), 0, span, kRsrcWord3);
 #pragma unroll
-  for (int ks = 0; ks < C::KSTEPS; ++ks)
-    qf[ks] = q_valid ? ld_global_16B(q + fbase + my_q * rs + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = buf_load16(rq, my_q * rsb + (ks * 16 + hh * 8) * 2);
+  }
 
   f32x16 o[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l0 = 0.f, l1 = 0.f;
 
   const int ntiles = (L + KT - 1) / KT;
-  const int vkq = tid % C::KQN, vch = tid / C::KQN;
+  const int last_valid = L - (ntiles - 1) * KT;  // keys in the last tile
 
-  u32x4 kreg[C::K_LD];
-  u32x4 vreg[C::KPT];
-  auto load_tile = [&](int j) {
-    const int key0 = j * KT;
+  // S^T for one tile (two 32-key blocks) from K buffer kb_. MFMA i uses the K
+  // operand (ks, kb) = (i/2, i%2); operands are read PF MFMAs ahead.
+  constexpr int PF = 4;
+  auto qk = [&](const unsigned char* kb_, f32x16& s0, f32x16& s1) {
+    constexpr int N = 2 * C::KSTEPS;
+    auto kload = [&](int i) {
+      return *reinterpret_cast<const u32x4*>(kb_ + (kaddr ^ ((i >> 1) << 5)) + (i & 1) * 32 * D * 2);
+    };
+    u32x4 ring[PF];
 #pragma unroll
-    for (int i = 0; i < C::K_LD; ++i) {
-      const int id = i * NT + tid, row = id / C::NCH, ch = id % C::NCH;
-      const int key = key0 + row;
-      kreg[i] = key < L ? ld_global_16B(k + fbase + key * rs + ch * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < PF; ++i) ring[i] = kload(i);
+    s0 = f32x16{};
+    s1 = f32x16{};
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int key = key0 + vkq * C::KPT + i;
-      vreg[i] = key < L ? ld_global_16B(v + fbase + key * rs + vch * 8) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* kb = smem + buf * C::BUF;
-    unsigned char* vb = kb + C::K_TILE;
-#pragma unroll
-    for (int i = 0; i < C::K_LD; ++i) {
-      const int id = i * NT + tid, row = id / C::NCH, ch = id % C::NCH;
-      *reinterpret_cast<u32x4*>(kb + k_off<D>(row, ch)) = kreg[i];
-    }
-    const int key_in = vkq * C::KPT;
-    const int kc = key_in >> 3, within = (key_in & 7) * 2;
-#pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      const int dv = vch * 8 + jd;
-      unsigned char* dst = vb + vt_off(dv, kc) + within;
-      if constexpr (C::KPT == 4) {
-        const uint32_t lo = bf16_elem(vreg[0], jd) | (bf16_elem(vreg[1], jd) << 16);
-        const uint32_t hi = bf16_elem(vreg[2], jd) | (bf16_elem(vreg[3], jd) << 16);
-        *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = bf16_elem(vreg[0], jd) | (bf16_elem(vreg[1], jd) << 16);
-      }
+    for (int i = 0; i < N; ++i) {
+      const u32x4 a = ring[i % PF];
+      if (i + PF < N) ring[i % PF] = kload(i + PF);
+      if (i & 1) s1 = mfma32x32x16(a, qf[i >> 1], s1);
+      else s0 = mfma32x32x16(a, qf[i >> 1], s0);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
+  // Rare paths below hold an empty volatile asm: it cannot be speculated, so
+  // the compiler keeps a real (uniform) branch instead of executing the path
+  // on every tile with selects.
+  auto mask_tail = [&](f32x16& s0, f32x16& s1) {
+    asm volatile("");
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 16 * (r >> 3) + 8 * hh + (r & 7);
+      if (key >= last_valid) s0[r] = -INFINITY;
+      if (key + 32 >= last_valid) s1[r] = -INFINITY;
+    }
+  };
+  auto tile_max = [&](const f32x16& s0, const f32x16& s1) {
+    float m = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(s0[r], s1[r]));
+    return max_across_halves(m) * c2;
+  };
+  auto rescale = [&](float mt) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
+      asm volatile("");
+      const float mn = fmaxf(m_run, mt);
+      const float f = __builtin_amdgcn_exp2f(m_run - mn);
+      l0 *= f;
+      l1 *= f;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) o[db] *= f;
+      m_run = mn;
+    }
+  };
+  auto softmax_p = [&](const f32x16& s0, const f32x16& s1, uint32_t* p0, uint32_t* p1) {
+    const float nm = -m_run;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float x0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, nm));
+      const float x1 = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c2, nm));
+      const float y0 = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, nm));
+      const float y1 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c2, nm));
+      a0 += x0; a1 += x1; a2 += y0; a3 += y1;
+      p0[r >> 1] = pack_bf16x2(x0, x1);
+      p1[r >> 1] = pack_bf16x2(y0, y1);
+    }
+    l0 += a0 + a1;
+    l1 += a2 + a3;
+  };
+  // O^T += V^T P^T. MFMA i: 16-key step ks = i/DB (block ks/2, half ks%2) and
+  // dv block db = i%DB; its V operand (two transposed reads) is read PF ahead.
+  auto pv = [&](const unsigned char* vb_, const uint32_t* p0, const uint32_t* p1) {
+    constexpr int N = 4 * C::DB;
+    auto vload = [&](int i) {
+      const int ks = i / C::DB, db = i % C::DB;
+      const int ra = 32 * (ks >> 1) + 16 * (ks & 1);
+      const u32x2 x0 = ds_read_tr16(vb_ + v_off(ra, db));
+      const u32x2 x1 = ds_read_tr16(vb_ + v_off(ra + 4, db));
+      return u32x4{x0[0], x0[1], x1[0], x1[1]};
+    };
+    u32x4 ring[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) ring[i] = vload(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int ks = i / C::DB, db = i % C::DB;
+      const u32x4 a = ring[i % PF];
+      if (i + PF < N) ring[i % PF] = vload(i + PF);
+      const uint32_t* p = (ks >> 1) ? p1 : p0;
+      const int hb = 4 * (ks & 1);
+      o[db] = mfma32x32x16(a, u32x4{p[hb], p[hb + 1], p[hb + 2], p[hb + 3]}, o[db]);
+    }
+  };
+
+  // ---- prologue: K_0, V_0, K_1 in flight, then S_0
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (ntiles > 1) issue_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16 sa0, sa1, sb0, sb1;
+  float mt_a = 0.f, mt_b = 0.f;
+  if (wave_active) {
+    qk(kbuf, sa0, sa1);
+    if (ntiles == 1 && last_valid < KT) mask_tail(sa0, sa1);
+    mt_a = tile_max(sa0, sa1);
+  }
+  __syncthreads();  // every wave has read K_0 before step 0 refills its buffer with K_2
 
-  const int r0 = pi32(lr), r1 = 32 + pi32(lr);
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+  // Step j (K runs one tile ahead of V): prefetch K_{j+2} and V_{j+1}; then
+  //   [S_{j+1} = K_{j+1} Q^T on MFMA]  beside  [P_j = exp2(S_j - m) on the VALU]
+  //   [O += V_j^T P_j^T on MFMA]       beside  [max of S_{j+1}]
+  // The flags are compile-time so that the steady-state loop has no branch
+  // between the two regions: P = j % 2 (LDS buffers), NEXT = tile j+1 exists,
+  // TAIL = tile j+1 may be the ragged last tile, LOADK = tile j+2 exists.
+  auto step = [&](auto flags, int j, f32x16& c0, f32x16& c1, float& mt_c, f32x16& n0, f32x16& n1,
+                  float& mt_n) {
+    using Fl = decltype(flags);
+    constexpr int P = Fl::P;
+    if constexpr (Fl::LOADK) issue_k(j + 2, P);
+    else if (j + 2 < ntiles) issue_k(j + 2, P);
+    if constexpr (Fl::NEXT) issue_v(j + 1, P ^ 1);
     if (wave_active) {
-      const unsigned char* kb = smem + buf * C::BUF;
-      const unsigned char* vb = kb + C::K_TILE;
-      // S^T = K Q^T for 64 keys x 32 queries
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        const int ch = 2 * ks + hh;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kb + k_off<D>(r0, ch));
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kb + k_off<D>(r1, ch));
-        s0 = mfma32x32x16(a0, qf[ks], s0);
-        s1 = mfma32x32x16(a1, qf[ks], s1);
-      }
-      const int nvalid = L - j * KT;
-      if (nvalid < KT) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 16 * (r >> 3) + 8 * hh + (r & 7);
-          if (key >= nvalid) s0[r] = -INFINITY;
-          if (key + 32 >= nvalid) s1[r] = -INFINITY;
-        }
-      }
-      float mt = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
-      mt = max_across_halves(mt) * c2;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
-        const float mn = fmaxf(m_run, mt);
-        const float f = __builtin_amdgcn_exp2f(m_run - mn);
-        l_run *= f;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[db] *= f;
-        m_run = mn;
-      }
-      const float nm = -m_run;
+      rescale(mt_c);
       uint32_t p0[8], p1[8];
-      float ls = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float a = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, nm));
-        const float bb = __builtin_amdgcn_exp2f(fmaf(s0[r + 1], c2, nm));
-        const float cc = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, nm));
-        const float dd = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c2, nm));
-        ls += (a + bb) + (cc + dd);
-        p0[r >> 1] = pack_bf16x2(a, bb);
-        p1[r >> 1] = pack_bf16x2(cc, dd);
-      }
-      l_run += ls;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const u32x4 pb0 = {p0[4 * half], p0[4 * half + 1], p0[4 * half + 2], p0[4 * half + 3]};
-        const u32x4 pb1 = {p1[4 * half], p1[4 * half + 1], p1[4 * half + 2], p1[4 * half + 3]};
-        const int kc0 = 2 * half + hh, kc1 = 4 + 2 * half + hh;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int dv = db * 32 + lr;
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(vb + vt_off(dv, kc0));
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(vb + vt_off(dv, kc1));
-          o[db] = mfma32x32x16(a0, pb0, o[db]);
-          o[db] = mfma32x32x16(a1, pb1, o[db]);
+      if constexpr (Fl::NEXT) {
+        qk(kbuf + (P ^ 1) * C::TILE, n0, n1);
+        softmax_p(c0, c1, p0, p1);
+        interleave<2 * C::KSTEPS, PF, 1, 7>();
+        if constexpr (Fl::TAIL) {
+          if (j + 2 == ntiles && last_valid < KT) mask_tail(n0, n1);
         }
+        pv(vbuf + P * C::TILE, p0, p1);
+        mt_n = tile_max(n0, n1);
+        interleave<4 * C::DB, PF, 2, 2>();
+      } else {
+        softmax_p(c0, c1, p0, p1);
+        pv(vbuf + P * C::TILE, p0, p1);
       }
     }
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  // flags: <P, NEXT, TAIL, LOADK>
+  using Main0 = StepFlags<0, true, false, true>;
+  using Main1 = StepFlags<1, true, false, true>;
+
+  int j = 0;
+  for (; j + 3 < ntiles; j += 2) {
+    step(Main0{}, j, sa0, sa1, mt_a, sb0, sb1, mt_b);
+    step(Main1{}, j + 1, sb0, sb1, mt_b, sa0, sa1, mt_a);
+  }
+  // Remaining 1 to 3 tiles, without the software pipeline (one score tile
+  // live): S_t is in sa, V_t in buffer t % 2, K_{t+1} in buffer (t+1) % 2.
+  for (int t = j; t < ntiles; ++t) {
+    const int pb = t & 1;
+    if (t + 1 < ntiles) issue_v(t + 1, pb ^ 1);
+    if (t + 2 < ntiles) issue_k(t + 2, pb);
+    if (wave_active) {
+      rescale(mt_a);
+      uint32_t p0[8], p1[8];
+      softmax_p(sa0, sa1, p0, p1);
+      pv(vbuf + pb * C::TILE, p0, p1);
+      if (t + 1 < ntiles) {
+        qk(kbuf + (pb ^ 1) * C::TILE, sa0, sa1);
+        if (t + 2 == ntiles && last_valid < KT) mask_tail(sa0, sa1);
+        mt_a = tile_max(sa0, sa1);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  // Epilogue: S_n -> LDS as bf16 S^T[dv][dk]; O = O / l + Q' S_n.
+  // ---- epilogue: S_n -> LDS as bf16 row-major [dk][dv]; O = O / l + Q' S_n
   const float* Sp = states + (long long)(b * H + h) * stride_bh + (long long)n * stride_frame;
-  for (int p = tid; p < D * D / 8; p += NT) {
-    const int dv4 = p % (D / 4), dkp = p / (D / 4);
-    const int dk = 2 * dkp, dv0 = 4 * dv4;
-    const f32x4 ra = *reinterpret_cast<const f32x4*>(Sp + dk * D + dv0);
-    const f32x4 rb = *reinterpret_cast<const f32x4*>(Sp + (dk + 1) * D + dv0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int dv = dv0 + i;
-      *reinterpret_cast<uint32_t*>(smem + st_off<D>(dv, dk >> 3) + (dk & 7) * 2) = pack_bf16x2(ra[i], rb[i]);
-    }
+  for (int p = tid; p < D * D / 4; p += NT) {
+    const int dk = p / (D / 4), dv0 = (p % (D / 4)) * 4;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(Sp + dk * D + dv0);
+    const int off = dk * (D * 2) + (((dv0 >> 3) ^ v_swz<NCH>(dk)) << 4) + (dv0 & 7) * 2;
+    *reinterpret_cast<u32x2*>(smem + off) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
   }
   __syncthreads();
   if (!wave_active) return;
 
-  const float inv = 1.f / sum_across_halves(l_run);
+  const __amdgpu_buffer_rsrc_t rqp = __builtin_amdgcn_make_buffer_rsrc((void*)(qp + fbase), 0, span, kRsrcWord3);
+  const float inv = 1.f / sum_across_halves(l0 + l1);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) o[db] *= inv;
 #pragma unroll
   for (int ks = 0; ks < C::KSTEPS; ++ks) {
-    const u32x4 bq = q_valid ? ld_global_16B(qp + fbase + my_q * rs + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
-    const int ch = 2 * ks + hh;
+    const u32x4 bq = buf_load16(rqp, my_q * rsb + (ks * 16 + hh * 8) * 2);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(smem + st_off<D>(db * 32 + lr, ch));
-      o[db] = mfma32x32x16(a, bq, o[db]);
+      const u32x2 x0 = ds_read_tr16(smem + v_off(16 * ks, db));
+      const u32x2 x1 = ds_read_tr16(smem + v_off(16 * ks + 4, db));
+      o[db] = mfma32x32x16(u32x4{x0[0], x0[1], x1[0], x1[1]}, bq, o[db]);
     }
   }
-  if (q_valid) {
-    uint16_t* op = out + fbase + my_q * rs;
+  if (my_q < L) {
+    uint16_t* op = out + fbase + (long long)my_q * H * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dv = db * 32 + 8 * g + 4 * hh;
-        st_global_8B(op + dv, u32x2{pack_bf16x2(o[db][4 * g], o[db][4 * g + 1]),
-                                    pack_bf16x2(o[db][4 * g + 2], o[db][4 * g + 3])});
+      for (int gg = 0; gg < 4; ++gg) {
+        const int dv = db * 32 + 8 * gg + 4 * hh;
+        st_global_8B(op + dv, u32x2{pack_bf16x2(o[db][4 * gg], o[db][4 * gg + 1]),
+                                    pack_bf16x2(o[db][4 * gg + 2], o[db][4 * gg + 3])});
       }
     }
   }

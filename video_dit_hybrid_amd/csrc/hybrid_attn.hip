@@ -36,6 +36,8 @@ ha_status check_shape(int B, int H, int T, int d, int L, int dtype, ha::Shape* s
   const long long items = (long long)B * H * (T / L) * ((L + 63) / 64);
   if (items > kMaxItems) return HA_ERR_SHAPE;
   if ((long long)B * H * (T / L) * 2 > kMaxItems) return HA_ERR_SHAPE;
+  // one (stream, head, frame) slab is addressed with 32-bit byte offsets
+  if (((long long)L * H * d + d) * 4 > kMaxItems) return HA_ERR_SHAPE;
   *s = ha::Shape{B, H, T, d, L, T / L};
   return HA_OK;
 }
@@ -65,10 +67,12 @@ ha_status run_readout(const void* q, const void* k, const void* v, const void* q
 ha_status run_update(const void* kp, const void* vp, const float* alpha, const float* beta,
                      float* state, float* snaps, float* gram, const ha::Shape& s, int dtype,
                      hipStream_t st) {
-  hipError_t e = dtype == HA_BF16 ? ha::launch_gram_bf16(kp, vp, beta, gram, s, st)
-                                  : ha::launch_gram_fp32(kp, vp, beta, gram, s, st);
-  if (e != hipSuccess) return HA_ERR_DEVICE;
-  return launched(ha::launch_state_scan(gram, alpha, state, snaps, s, st));
+  if (dtype == HA_BF16) {
+    if (ha::launch_gram_bf16(kp, vp, beta, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
+    return launched(ha::launch_state_scan_bf16(gram, alpha, state, snaps, s, st));
+  }
+  if (ha::launch_gram_fp32(kp, vp, beta, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  return launched(ha::launch_state_scan_fp32(gram, alpha, state, snaps, s, st));
 }
 
 }  // namespace

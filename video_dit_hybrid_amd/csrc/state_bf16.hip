@@ -26,8 +26,10 @@ __device__ __forceinline__ int swz8(int i) { return (i & 7) ^ ((i >> 3) & 1); }
 // [D rows][TC tokens] bf16, 16-byte chunks of 8 tokens, XOR-swizzled by row.
 __device__ __forceinline__ int tt_off(int row, int kc) { return row * (TC * 2) + ((kc ^ swz8(row)) << 4); }
 
-// grid: B*H*F*2 work-groups; work-group (hf, half) computes the d x d block
-// half of [G | B] for one (b, h, frame), contracting over the frame's tokens.
+// grid: B*H*F*2 work-groups; work-group (hf, half) computes G (half 0) or B
+// (half 1) for one (b, h, frame), contracting over the frame's tokens. G is
+// stored negated and split into bf16 hi + lo planes, ready to be the A
+// operand of the scan's MFMA; B is stored in fp32.
 template <int D>
 __global__ __launch_bounds__(NT, 2) void gram_bf16_kernel(
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -117,7 +119,12 @@ __global__ __launch_bounds__(NT, 2) void gram_bf16_kernel(
     }
   }
 
-  float* g = gram + ((long long)(b * H + h) * F + n) * (long long)D * 2 * D + half * D;
+  // workspace per (b, h, frame): [-G hi: D x D bf16][-G lo: D x D bf16][B: D x D fp32]
+  unsigned char* base = reinterpret_cast<unsigned char*>(gram) +
+                        ((size_t)(b * H + h) * F + n) * (size_t)D * D * 8;
+  uint16_t* gh = reinterpret_cast<uint16_t*>(base);
+  uint16_t* gl = gh + (size_t)D * D;
+  float* bo = reinterpret_cast<float*>(base + (size_t)D * D * 4);
 #pragma unroll
   for (int blk = 0; blk < NBLK; ++blk) {
     const int id = wave * NBLK + blk;
@@ -125,7 +132,15 @@ __global__ __launch_bounds__(NT, 2) void gram_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = rb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      g[(long long)i * 2 * D + cb * 32 + lr] = acc[blk][r];
+      const size_t o = (size_t)i * D + cb * 32 + lr;
+      if (half) {
+        bo[o] = acc[blk][r];
+      } else {
+        const float x = -acc[blk][r];
+        const uint32_t hi = pack_bf16x2(x, 0.f) & 0xffffu;
+        gh[o] = (uint16_t)hi;
+        gl[o] = (uint16_t)(pack_bf16x2(x - __uint_as_float(hi << 16), 0.f) & 0xffffu);
+      }
     }
   }
 }
