@@ -53,7 +53,6 @@ constexpr int NW = 4;           // waves per work-group
 constexpr int QPB = QPW * NW;   // queries per work-group
 constexpr int NT = NW * kWave;  // threads per work-group
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
 
 template <int D>
 struct Cfg {
@@ -67,9 +66,6 @@ struct Cfg {
   static_assert(NLD >= 1, "tile too small for the load split");
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-__device__ __forceinline__ lds_ptr_t lds_ptr(void* p) { return (lds_ptr_t)p; }
-
 __device__ __forceinline__ int pi32(int i) {  // swap bits 2 and 3
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
@@ -82,37 +78,9 @@ __device__ __forceinline__ int k_swz(int row) {
   if constexpr (NCH >= 16) return i & 15;
   else return (i & 7) ^ ((i >> 3) & 1);
 }
-// V tile [KT][D] (and S [D][D]) read by ds_read_b64_tr_b16: 32 lanes (one
-// 256-byte LDS cycle) read 4 consecutive rows x 64 bytes, i.e. four aligned
-// 16-byte chunks per row; XOR-ing the chunk index with 4*(row%4) puts the four
-// rows on disjoint 64-byte bank groups (measured conflict-free on gfx950).
+// V tile [KT][D] and S [D][D] are read with ds_read_tr16 (see tr_swz).
 template <int NCH>
-__device__ __forceinline__ int v_swz(int row) {
-  if constexpr (NCH >= 16) return 4 * (row & 3) + 2 * ((row >> 3) & 1);
-  else return 2 * (row & 3);
-}
-
-__device__ __forceinline__ u32x2 ds_read_tr16(const unsigned char* p) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(lds_ptr((void*)p)));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// 16 bytes per lane, global (buffer) -> LDS without passing through VGPRs:
-// lane l writes LDS bytes [lds + 16*l, lds + 16*l + 16). The range check of the
-// descriptor covers voff + soff; out-of-range lanes write zeros. The builtin is
-// only compiled in the device pass: clang's host pass drops the host handle of
-// a kernel template whose body names it.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 16, voff, soff, 0, 0);
-#endif
-}
-
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
+__device__ __forceinline__ int v_swz(int row) { return tr_swz<NCH>(row); }
 
 // Scheduling groups for the preceding code of the same basic block (mask: 0x8
 // MFMA, 0x100 LDS read, 0x402 VALU incl. transcendental): PF*R reads first,
@@ -190,13 +158,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     const uint32_t toff = (uint32_t)j * KT * rsb;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16(rk, kbuf + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
+      dma16_to_lds(rk, kbuf + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
   };
   auto issue_v = [&](int j, int buf) {
     const uint32_t toff = (uint32_t)j * KT * rsb;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16(rv, vbuf + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
+      dma16_to_lds(rv, vbuf + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
   };
 
   // ---- per-lane LDS read offsets

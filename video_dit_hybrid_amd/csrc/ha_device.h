@@ -58,6 +58,67 @@ __device__ __forceinline__ void st_global_8B(void* p, u32x2 v) {
   *reinterpret_cast<u32x2*>(p) = v;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t lds_ptr(void* p) { return (lds_ptr_t)p; }
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor word 3, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcWord3);
+}
+
+// Eight bytes per lane from LDS with a 16-bit transpose inside each group of
+// 16 lanes: lanes that read a 4-row x 16-column bf16 block row-wise (4 lanes
+// per row, 8 bytes each) receive one column each, its 4 rows in order.
+__device__ __forceinline__ u32x2 ds_read_tr16(const unsigned char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(lds_ptr((void*)p)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Global (buffer) -> LDS without passing through VGPRs: lane l writes LDS bytes
+// [lds + n*l, lds + n*l + n) for n = 16 or 4 bytes. The descriptor's range check covers
+// voff + soff; out-of-range lanes write zeros. The builtin is only compiled in
+// the device pass: clang's host pass drops the host handle of a kernel
+// template whose body names it.
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 16, voff, soff, 0, 0);
+#endif
+}
+__device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 4, voff, soff, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Row-major [rows][D] bf16 tiles read with ds_read_tr16: 32 lanes (one 256-byte
+// LDS cycle) read 4 consecutive rows x 64 bytes; XOR-ing the 16-byte chunk index
+// with this value puts the four rows on disjoint bank groups (conflict-free on
+// gfx950 as measured with the bank-conflict counter).
+template <int NCH>
+__device__ __forceinline__ int tr_swz(int row) {
+  if constexpr (NCH >= 16) return 4 * (row & 3) + 2 * ((row >> 3) & 1);
+  else return 2 * (row & 3);
+}
+
+// Work-group barrier that orders LDS only. __syncthreads() also waits for every
+// outstanding global load of the wave (its release fence), which would drain
+// register prefetches issued for later steps; this waits for the wave's LDS
+// operations (lgkmcnt = 0; vmcnt and expcnt left at their maxima) and keeps
+// the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Work-group index -> work item, so that consecutive work items land on the
 // same XCD (work-groups are dealt to the 8 XCDs round-robin, and each XCD has
 // its own L2). Requires gridDim.x % 8 == 0; items >= n_items are padding.

@@ -20,126 +20,170 @@ namespace ha {
 namespace {
 
 constexpr int TC = 64;   // tokens per LDS chunk
-constexpr int NT = 256;  // threads per work-group
+constexpr int NW = 8;    // waves per work-group
+constexpr int NT = NW * kWave;
 
-__device__ __forceinline__ int swz8(int i) { return (i & 7) ^ ((i >> 3) & 1); }
-// [D rows][TC tokens] bf16, 16-byte chunks of 8 tokens, XOR-swizzled by row.
-__device__ __forceinline__ int tt_off(int row, int kc) { return row * (TC * 2) + ((kc ^ swz8(row)) << 4); }
-
-// grid: B*H*F*2 work-groups; work-group (hf, half) computes G (half 0) or B
-// (half 1) for one (b, h, frame), contracting over the frame's tokens. G is
-// stored negated and split into bf16 hi + lo planes, ready to be the A
-// operand of the scan's MFMA; B is stored in fp32.
+// grid: one work-group per (b, h, frame). Waves 0-3 compute G = K'^T diag(beta)
+// K', waves 4-7 compute B = K'^T diag(beta) V', each wave a 32-row band of the
+// d x d result, contracting over the frame's tokens in chunks of 64.
+//
+// The K', V' chunks arrive row-major ([token][d] bf16, as stored) by direct
+// global -> LDS loads, two chunks in flight, and beta by a 4-byte-per-lane load;
+// tokens >= L are outside the buffer descriptors' range and arrive as zeros.
+// Both MFMA operands need 8 consecutive tokens per lane, which transposed LDS
+// reads deliver without any transposing write. The A operand beta*K' is formed
+// in fp32 in registers and split into bf16 hi + lo (two MFMAs), which keeps
+// ~16 mantissa bits; K' and V' themselves are exact in bf16.
+//
+// Output, per (b, h, frame): -G as bf16 hi + lo and B as fp32, laid out in the
+// scan's MFMA fragment order (see the stores at the end).
 template <int D>
-__global__ __launch_bounds__(NT, 2) void gram_bf16_kernel(
-    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
-    const float* __restrict__ beta, float* __restrict__ gram, int H, int T, int L, int F) {
-  constexpr int NCH = D / 8;        // 16-byte chunks in a row of D bf16
-  constexpr int KPT = NCH / 4;      // tokens per thread in the transposing load
-  constexpr int KQN = NT / NCH;     // token groups
-  constexpr int RB = D / 32;        // 32-row blocks of the output
-  constexpr int NBLK = RB * RB / 4; // output blocks per wave
-  constexpr int TILE = D * TC * 2;  // bytes of one transposed operand tile
-  static_assert(KQN * KPT == TC, "transpose must cover the chunk");
-  __shared__ __align__(16) unsigned char smem[3 * TILE];
-  unsigned char* a_hi = smem;
-  unsigned char* a_lo = smem + TILE;
-  unsigned char* b_t = smem + 2 * TILE;
+__global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restrict__ kp,
+                                                       const uint16_t* __restrict__ vp,
+                                                       const float* __restrict__ beta,
+                                                       float* __restrict__ gram, int H, int T, int L,
+                                                       int F) {
+  constexpr int NCH = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE = TC * D * 2;           // bytes of one K' or V' chunk
+  constexpr int BUF = 2 * TILE + TC * 4;     // K', V', beta
+  constexpr int SEGS = TILE / 1024;          // 1 KB direct-to-LDS segments per tile
+  constexpr int RPS = 64 / NCH;              // rows per segment
+  constexpr int NRB = D / 32;                // 32-row (and -column) blocks
+  constexpr int NB = NRB * NRB / 4;          // output blocks per wave
+  static_assert(SEGS % NW == 0 || SEGS == NW, "segment split");
+  static_assert(NB == NRB || NB == 1, "a wave's blocks share one row band");
+  __shared__ __align__(16) unsigned char smem[2 * BUF];
 
-  const int half = blockIdx.x & 1;
-  const int hf = blockIdx.x >> 1;
+  const int hf = blockIdx.x;
   const int h = hf % H;
   const int n = (hf / H) % F;
   const int b = hf / (H * F);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
-  const long long rs = (long long)H * D;
-  const long long fbase = ((long long)b * T + (long long)n * L) * rs + (long long)h * D;
-  const float* bbase = beta + ((long long)b * T + (long long)n * L) * H + h;
-  const uint16_t* src_b = half ? vp : kp;
+  const int half = wave >> 2;                 // 0: G, 1: B
+  const int q0 = (wave & 3) * NB;             // first block index within the half
+  const int rb = q0 / NRB;                    // row band (shared by the wave's blocks)
 
-  const int tq = tid % KQN, tch = tid / KQN;
+  const uint32_t rsb = (uint32_t)H * D * 2;
+  const long long fbase = ((long long)b * T + (long long)n * L) * ((long long)H * D) + (long long)h * D;
+  const int span = (int)((uint32_t)(L - 1) * rsb + D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + fbase, span);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + fbase, span);
+  const __amdgpu_buffer_rsrc_t rbeta =
+      make_rsrc(beta + ((long long)b * T + (long long)n * L) * H + h, (int)(((uint32_t)(L - 1) * H + 1) * 4));
 
-  f32x16 acc[NBLK];
+  // direct-to-LDS: wave w fills segments w, w + NW, ... of each tile; those are
+  // NW*RPS rows apart, which leaves the transposed-read swizzle unchanged.
+  constexpr int MY_SEGS = SEGS / NW;
+  const int srow = wave * RPS + lane / NCH, spc = lane % NCH;
+  const uint32_t soff = srow * rsb + ((spc ^ tr_swz<NCH>(srow)) << 4);
+  auto issue = [&](int c, int buf) {
+    unsigned char* base = smem + buf * BUF;
+    const uint32_t toff = (uint32_t)c * TC * rsb;
 #pragma unroll
-  for (int i = 0; i < NBLK; ++i) acc[i] = f32x16{};
-
-  for (int t0 = 0; t0 < L; t0 += TC) {
-    u32x4 kr[KPT], br[KPT];
-    float be[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int t = t0 + tq * KPT + i;
-      const bool ok = t < L;
-      kr[i] = ok ? ld_global_16B(kp + fbase + t * rs + tch * 8) : u32x4{0, 0, 0, 0};
-      br[i] = ok ? (half ? ld_global_16B(src_b + fbase + t * rs + tch * 8) : kr[i]) : u32x4{0, 0, 0, 0};
-      be[i] = ok ? bbase[(long long)t * H] : 0.f;
+    for (int i = 0; i < MY_SEGS; ++i) {
+      const uint32_t so = toff + (uint32_t)i * NW * RPS * rsb;
+      dma16_to_lds(rk, base + (wave + NW * i) * 1024, soff, so);
+      dma16_to_lds(rv, base + TILE + (wave + NW * i) * 1024, soff, so);
     }
-    __syncthreads();  // previous chunk's operand reads are done
-    const int tin = tq * KPT, kc = tin >> 3, within = (tin & 7) * 2;
+    if (wave == 0) dma4_to_lds(rbeta, base + 2 * TILE, (uint32_t)lane * H * 4, (uint32_t)c * TC * H * 4);
+  };
+
+  // transposed-read offsets: 16-lane group g reads rows 8*hh + gi/4 (+4) of a
+  // 16-token step, columns 16*(g%2) + 4*(gi%4) of a 32-column block
+  const int gi = lane & 15, g = lane >> 4;
+  const int vrow = 8 * hh + (gi >> 2);
+  const int vsw = tr_swz<NCH>(vrow);
+  const int vcol = 16 * (g & 1) + 4 * (gi & 3);
+  auto tr_off = [&](int row_add, int cblk) {
+    const int col = vcol + 32 * cblk;
+    return (vrow + row_add) * (D * 2) + (((col >> 3) ^ vsw) << 4) + (col & 7) * 2;
+  };
+  auto tr8 = [&](const unsigned char* tile, int ks, int cblk) {
+    const u32x2 x0 = ds_read_tr16(tile + tr_off(16 * ks, cblk));
+    const u32x2 x1 = ds_read_tr16(tile + tr_off(16 * ks + 4, cblk));
+    return u32x4{x0[0], x0[1], x1[0], x1[1]};
+  };
+
+  f32x16 acc[NB];
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      const int row = tch * 8 + jd;
-      uint32_t wb[KPT / 2], wh[KPT / 2], wl[KPT / 2];
-#pragma unroll
-      for (int i = 0; i < KPT; i += 2) {
-        wb[i / 2] = bf16_elem(br[i], jd) | (bf16_elem(br[i + 1], jd) << 16);
-        const float x0 = be[i] * __uint_as_float(bf16_elem(kr[i], jd) << 16);
-        const float x1 = be[i + 1] * __uint_as_float(bf16_elem(kr[i + 1], jd) << 16);
-        const uint32_t hi = pack_bf16x2(x0, x1);
-        wh[i / 2] = hi;
-        wl[i / 2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
-      }
-      const int off = tt_off(row, kc) + within;
-      if constexpr (KPT == 4) {
-        *reinterpret_cast<u32x2*>(b_t + off) = u32x2{wb[0], wb[1]};
-        *reinterpret_cast<u32x2*>(a_hi + off) = u32x2{wh[0], wh[1]};
-        *reinterpret_cast<u32x2*>(a_lo + off) = u32x2{wl[0], wl[1]};
-      } else {
-        *reinterpret_cast<uint32_t*>(b_t + off) = wb[0];
-        *reinterpret_cast<uint32_t*>(a_hi + off) = wh[0];
-        *reinterpret_cast<uint32_t*>(a_lo + off) = wl[0];
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < NB; ++i) acc[i] = f32x16{};
+
+  const int nch = (L + TC - 1) / TC;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) issue(c + 1, buf ^ 1);
+    const unsigned char* kt = smem + buf * BUF;
+    const unsigned char* bt = half ? kt + TILE : kt;
+    const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
 #pragma unroll
     for (int ks = 0; ks < TC / 16; ++ks) {
-      const int kcr = 2 * ks + hh;
+      // A = (beta K')^T rows 32*rb.., tokens 16*ks + 8*hh + e: split hi + lo
+      const u32x4 kraw = tr8(kt, ks, rb);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(be + 16 * ks + 8 * hh);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(be + 16 * ks + 8 * hh + 4);
+      u32x4 ahi, alo;
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) {
-        const int id = wave * NBLK + blk;
-        const int rb = id / RB, cb = id % RB;
-        const int ra = rb * 32 + lr, rbt = cb * 32 + lr;
-        const u32x4 ah = *reinterpret_cast<const u32x4*>(a_hi + tt_off(ra, kcr));
-        const u32x4 al = *reinterpret_cast<const u32x4*>(a_lo + tt_off(ra, kcr));
-        const u32x4 bt = *reinterpret_cast<const u32x4*>(b_t + tt_off(rbt, kcr));
-        acc[blk] = mfma32x32x16(ah, bt, acc[blk]);
-        acc[blk] = mfma32x32x16(al, bt, acc[blk]);
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float bl = w2 < 2 ? b0[2 * w2] : b1[2 * w2 - 4];
+        const float bu = w2 < 2 ? b0[2 * w2 + 1] : b1[2 * w2 - 3];
+        const float x0 = bl * bf16_lo_to_f32(kraw[w2]);
+        const float x1 = bu * bf16_hi_to_f32(kraw[w2]);
+        const uint32_t hi = pack_bf16x2(x0, x1);
+        ahi[w2] = hi;
+        alo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const u32x4 bop = tr8(bt, ks, (q0 + i) % NRB);
+        acc[i] = mfma32x32x16(ahi, bop, acc[i]);
+        acc[i] = mfma32x32x16(alo, bop, acc[i]);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
-  // workspace per (b, h, frame): [-G hi: D x D bf16][-G lo: D x D bf16][B: D x D fp32]
+  // Workspace per (b, h, frame), in the scan's MFMA fragment order:
+  //   G hi : [band i (NRB)][k-step (D/16)][lane] 16 bytes  (8 bf16 of -G)
+  //   G lo : the same for the low halves
+  //   B    : [col block (NRB)][row band (NRB)][lane] 64 bytes (16 fp32)
+  // G is symmetric, so the accumulator registers [8s, 8s+8) of the block
+  // (row band kb, column block rb) are the scan's A fragment of -G for output
+  // band rb and k-step 2*kb + s, under the contraction order in which k-slot
+  // 8*hh + e of that step is k = 32*kb + 16*s + 8*(e/4) + 4*hh + e%4.
   unsigned char* base = reinterpret_cast<unsigned char*>(gram) +
                         ((size_t)(b * H + h) * F + n) * (size_t)D * D * 8;
-  uint16_t* gh = reinterpret_cast<uint16_t*>(base);
-  uint16_t* gl = gh + (size_t)D * D;
-  float* bo = reinterpret_cast<float*>(base + (size_t)D * D * 4);
+  constexpr int KS = D / 16;
+  u32x4* ghi = reinterpret_cast<u32x4*>(base);
+  u32x4* glo = reinterpret_cast<u32x4*>(base + (size_t)D * D * 2);
+  f32x4* bfr = reinterpret_cast<f32x4*>(base + (size_t)D * D * 4);
 #pragma unroll
-  for (int blk = 0; blk < NBLK; ++blk) {
-    const int id = wave * NBLK + blk;
-    const int rb = id / RB, cb = id % RB;
+  for (int i = 0; i < NB; ++i) {
+    const int cb = (q0 + i) % NRB;
+    if (half) {
+      f32x4* dst = bfr + ((size_t)(cb * NRB + rb) * 64 + lane) * 4;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = rb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const size_t o = (size_t)i * D + cb * 32 + lr;
-      if (half) {
-        bo[o] = acc[blk][r];
-      } else {
-        const float x = -acc[blk][r];
-        const uint32_t hi = pack_bf16x2(x, 0.f) & 0xffffu;
-        gh[o] = (uint16_t)hi;
-        gl[o] = (uint16_t)(pack_bf16x2(x - __uint_as_float(hi << 16), 0.f) & 0xffffu);
+      for (int v4 = 0; v4 < 4; ++v4)
+        dst[v4] = f32x4{acc[i][4 * v4], acc[i][4 * v4 + 1], acc[i][4 * v4 + 2], acc[i][4 * v4 + 3]};
+    } else {
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        u32x4 hi, lo;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const float x0 = -acc[i][8 * sh + 2 * w2], x1 = -acc[i][8 * sh + 2 * w2 + 1];
+          const uint32_t hp = pack_bf16x2(x0, x1);
+          hi[w2] = hp;
+          lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
+        }
+        const size_t fo = (size_t)(cb * KS + 2 * rb + sh) * 64 + lane;
+        ghi[fo] = hi;
+        glo[fo] = lo;
       }
     }
   }
@@ -149,7 +193,7 @@ __global__ __launch_bounds__(NT, 2) void gram_bf16_kernel(
 
 hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, float* gram,
                             const Shape& s, hipStream_t st) {
-  const long long groups = (long long)s.B * s.H * s.F * 2;
+  const long long groups = (long long)s.B * s.H * s.F;
   if (s.d == 128)
     gram_bf16_kernel<128><<<(int)groups, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta,
                                                       gram, s.H, s.T, s.L, s.F);

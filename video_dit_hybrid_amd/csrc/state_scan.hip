@@ -7,14 +7,18 @@
 //
 // bf16 path (state_scan_mfma_kernel): the block is 32 columns; wave w keeps
 // rows [32w, 32w+32) of it in MFMA accumulators (fp32) for the whole walk.
-// Per step: S_{n-1} is split into bf16 hi + lo and written transposed to LDS;
-// the accumulators are set to alpha S_{n-1} + B_n; then
+// Per step: S_{n-1} is split into bf16 hi + lo and shared through LDS as MFMA
+// B fragments (the accumulator layout already is one, in the contraction order
+// the gram kernel writes -G in); the accumulators are set to
+// alpha S_{n-1} + B_n; then
 // acc += (-G)_hi S_hi + (-G)_hi S_lo + (-G)_lo S_hi on MFMA, which keeps the
 // product fp32-accurate (~16 mantissa bits per operand). The operands of step
-// n+1 (G rows, B block, alpha) are loaded while step n computes.
+// n+2 (G rows, B block, alpha) are loaded while step n computes.
 //
 // fp32 path (state_scan_fp32_kernel): the block is 16 columns in LDS and the
 // product is plain fp32 FMA, for callers whose inputs are fp32.
+#include <type_traits>
+
 #include "ha_device.h"
 #include "ha_launch.h"
 
@@ -25,27 +29,26 @@ namespace {
 constexpr int CWM = 32;   // state columns per work-group
 constexpr int NTM = 256;  // 4 waves, one 32-row block each (D = 128); D = 64 uses 2 waves
 
-__device__ __forceinline__ int sw8(int i) { return (i & 7) ^ ((i >> 3) & 1); }
-
 template <int D>
 __global__ __launch_bounds__(NTM) void state_scan_mfma_kernel(const unsigned char* __restrict__ ws,
                                                               const float* __restrict__ alpha,
                                                               float* __restrict__ state,
                                                               float* __restrict__ snaps, int H,
                                                               int F) {
+  constexpr int NRB = D / 32;                       // 32-row bands (= waves in use)
   constexpr int NCB = D / CWM;
   constexpr int KS = D / 16;                        // k-steps over d_k
   constexpr size_t PER = (size_t)D * D * 8;         // workspace bytes per (b, h, frame)
-  constexpr int SROW = D * 2;                       // bytes of one S^T row (D bf16)
-  // S^T[j][k] hi and lo planes, double buffered: 2 * 2 * CWM * D * 2 bytes
-  __shared__ __align__(16) unsigned char lds[2][2][CWM * SROW];
+  // S operand fragments [k-step][lane] 16 bytes, hi and lo planes, double buffered
+  __shared__ __align__(16) u32x4 lds[2][2][KS][64];
 
   const int cb = blockIdx.x % NCB;
   const int bh = blockIdx.x / NCB;
   const int h = bh % H, b = bh / H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
-  const bool active = wave < D / 32;
+  const bool active = wave < NRB;
   const int row0 = wave * 32;
   const int col = cb * CWM + lr;
 
@@ -58,70 +61,81 @@ __global__ __launch_bounds__(NTM) void state_scan_mfma_kernel(const unsigned cha
     for (int r = 0; r < 16; ++r) acc[r] = sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col];
   }
 
-  // operands of one step: rows row0.. of -G (hi, lo) as A fragments, B block, alpha
-  u32x4 gh[KS], gl[KS];
-  float bv[16];
-  float al = 0.f;
-  auto fetch = [&](int n) {
+  // operands of one step (-G hi and lo A fragments of this band, the B block,
+  // alpha) in a two-slot ring: step n's operands are requested two steps
+  // earlier. Each request is one contiguous 1 KB per wave (fragment order).
+  u32x4 gh[2][KS], gl[2][KS];
+  f32x4 bv[2][4];
+  float al[2] = {0.f, 0.f};
+  auto fetch = [&](int slot, int n) {
     const unsigned char* base = ws + ((size_t)bh * F + n) * PER;
-    const uint16_t* ghp = reinterpret_cast<const uint16_t*>(base);
-    const uint16_t* glp = ghp + (size_t)D * D;
-    const float* bp = reinterpret_cast<const float*>(base + (size_t)D * D * 4);
+    const u32x4* ghp = reinterpret_cast<const u32x4*>(base) + (size_t)wave * KS * 64 + lane;
+    const u32x4* glp = reinterpret_cast<const u32x4*>(base + (size_t)D * D * 2) + (size_t)wave * KS * 64 + lane;
+    const f32x4* bp = reinterpret_cast<const f32x4*>(base + (size_t)D * D * 4) + ((size_t)(cb * NRB + wave) * 64 + lane) * 4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const size_t off = (size_t)(row0 + lr) * D + ks * 16 + hh * 8;
-      gh[ks] = ld_global_16B(ghp + off);
-      gl[ks] = ld_global_16B(glp + off);
+      gh[slot][ks] = ghp[ks * 64];
+      gl[slot][ks] = glp[ks * 64];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bv[r] = bp[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col];
-    al = alpha[((size_t)b * F + n) * H + h];
+    for (int v4 = 0; v4 < 4; ++v4) bv[slot][v4] = bp[v4];
+    al[slot] = alpha[((size_t)b * F + n) * H + h];
   };
-  if (active) fetch(0);
+  if (active) {
+    fetch(0, 0);
+    if (F > 1) fetch(1, 1);
+  }
 
-  for (int n = 0; n < F; ++n) {
-    const int buf = n & 1;
+  // one frame; slot == n % 2 (also the LDS buffer), fixed at compile time
+  auto step = [&](auto slot_c, int n) {
+    constexpr int SL = decltype(slot_c)::value;
     if (active) {
-      // S_{n-1}: snapshot out, and hi/lo split into S^T in LDS
-      if (snaps) {
+      if (snaps) {  // S_{n-1}, the state frame n's readout reads
         float* dst = snaps + ((size_t)bh * F + n) * D * D;
 #pragma unroll
         for (int r = 0; r < 16; ++r) dst[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
       }
+      // this band's rows of S_{n-1} are the B fragments of k-steps 2*wave, 2*wave+1
+      // (same contraction order as the -G fragments): registers [8s, 8s+8)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int k0 = row0 + 8 * g + 4 * hh;  // four consecutive rows of S = four k of S^T
-        const uint32_t h01 = pack_bf16x2(acc[4 * g], acc[4 * g + 1]);
-        const uint32_t h23 = pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3]);
-        const uint32_t l01 = pack_bf16x2(acc[4 * g] - bf16_lo_to_f32(h01), acc[4 * g + 1] - bf16_hi_to_f32(h01));
-        const uint32_t l23 = pack_bf16x2(acc[4 * g + 2] - bf16_lo_to_f32(h23), acc[4 * g + 3] - bf16_hi_to_f32(h23));
-        const int off = lr * SROW + (((k0 >> 3) ^ sw8(lr)) << 4) + (k0 & 7) * 2;
-        *reinterpret_cast<u32x2*>(&lds[buf][0][off]) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(&lds[buf][1][off]) = u32x2{l01, l23};
+      for (int sh = 0; sh < 2; ++sh) {
+        u32x4 hi, lo;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const float x0 = acc[8 * sh + 2 * w2], x1 = acc[8 * sh + 2 * w2 + 1];
+          const uint32_t hp = pack_bf16x2(x0, x1);
+          hi[w2] = hp;
+          lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
+        }
+        lds[SL][0][2 * wave + sh][lane] = hi;
+        lds[SL][1][2 * wave + sh][lane] = lo;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (active) {
       f32x16 nacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) nacc[r] = fmaf(al, acc[r], bv[r]);
-      u32x4 cgh[KS], cgl[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) { cgh[ks] = gh[ks]; cgl[ks] = gl[ks]; }
-      if (n + 1 < F) fetch(n + 1);
+      for (int r = 0; r < 16; ++r) nacc[r] = fmaf(al[SL], acc[r], bv[SL][r >> 2][r & 3]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int kc = 2 * ks + hh;
-        const int off = lr * SROW + ((kc ^ sw8(lr)) << 4);
-        const u32x4 shi = *reinterpret_cast<const u32x4*>(&lds[buf][0][off]);
-        const u32x4 slo = *reinterpret_cast<const u32x4*>(&lds[buf][1][off]);
-        nacc = mfma32x32x16(cgh[ks], shi, nacc);
-        nacc = mfma32x32x16(cgh[ks], slo, nacc);
-        nacc = mfma32x32x16(cgl[ks], shi, nacc);
+        const u32x4 shi = lds[SL][0][ks][lane];
+        const u32x4 slo = lds[SL][1][ks][lane];
+        nacc = mfma32x32x16(gh[SL][ks], shi, nacc);
+        nacc = mfma32x32x16(gh[SL][ks], slo, nacc);
+        nacc = mfma32x32x16(gl[SL][ks], shi, nacc);
       }
+      if (n + 2 < F) fetch(SL, n + 2);
       acc = nacc;
     }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int n = 0;
+  for (; n + 1 < F; n += 2) {
+    step(S0{}, n);
+    step(S1{}, n + 1);
   }
+  if (n < F) step(S0{}, n);
   if (active) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
