@@ -31,7 +31,8 @@ METRIC = "hybrid-attn frames/sec + % bf16 MFMA peak, 480p Wan-1.3B shape, 1 MI35
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_480p_traffic.txt")
-ATTN_SOURCE = os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", "attn_bf16.hip")
+# the attention kernel's sources: the counter summary is valid only for these exact bytes
+ATTN_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("attn_bf16.hip", "ha_device.h")]
 
 
 def log(*a):
@@ -48,6 +49,13 @@ def flops(w):
     return att, rd, upd
 
 
+def attn_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
 def traffic_for_current_kernel():
     """HBM bytes per launch of the attention kernel from the committed rocprofv3
     counter summary, or None when the kernel source changed since it was taken."""
@@ -58,7 +66,7 @@ def traffic_for_current_kernel():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
+    src_hash = attn_source_hash()
     if kv.get("kernel_source_sha256_16") != src_hash:
         return None
     try:
