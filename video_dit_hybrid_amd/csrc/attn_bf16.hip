@@ -108,8 +108,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ qp,
     const float* __restrict__ states, long long stride_bh, long long stride_frame,
-    uint16_t* __restrict__ out, int H, int T, int L, int F, int qtiles, int n_items,
-    float c2 /* softmax scale * log2(e) */) {
+    const unsigned char* __restrict__ sfrag, uint16_t* __restrict__ out, int H, int T, int L, int F,
+    int qtiles, int n_items, float c2 /* softmax scale * log2(e) */) {
   using C = Cfg<D>;
   constexpr int NCH = C::NCH;
   __shared__ __align__(16) unsigned char smem[C::SMEM];
@@ -371,29 +371,74 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: S_n -> LDS as bf16 row-major [dk][dv]; O = O / l + Q' S_n
-  const float* Sp = states + (long long)(b * H + h) * stride_bh + (long long)n * stride_frame;
-  for (int p = tid; p < D * D / 4; p += NT) {
-    const int dk = p / (D / 4), dv0 = (p % (D / 4)) * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(Sp + dk * D + dv0);
-    const int off = dk * (D * 2) + (((dv0 >> 3) ^ v_swz<NCH>(dk)) << 4) + (dv0 & 7) * 2;
-    *reinterpret_cast<u32x2*>(smem + off) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-  }
-  __syncthreads();
-  if (!wave_active) return;
-
+  // ---- epilogue: O = O / l + Q' S_n. S_n reaches LDS either as the bf16
+  // readout fragments the state scan wrote (copied as they are), or from the
+  // fp32 row-major state, converted here to bf16 [dk][dv].
   const __amdgpu_buffer_rsrc_t rqp = __builtin_amdgcn_make_buffer_rsrc((void*)(qp + fbase), 0, span, kRsrcWord3);
-  const float inv = 1.f / sum_across_halves(l0 + l1);
+  if (sfrag) {
+    constexpr int NSEG = D * D * 2 / 1024;  // 1 KB fragments
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(sfrag + ((size_t)(b * H + h) * F + n) * (size_t)D * D * 2, D * D * 2);
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) o[db] *= inv;
+    for (int i = wave; i < NSEG; i += NW) dma16_to_lds(rs, smem + i * 1024, lane * 16, i * 1024);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!wave_active) return;
+    const float inv = 1.f / sum_across_halves(l0 + l1);
 #pragma unroll
-  for (int ks = 0; ks < C::KSTEPS; ++ks) {
-    const u32x4 bq = buf_load16(rqp, my_q * rsb + (ks * 16 + hh * 8) * 2);
+    for (int db = 0; db < C::DB; ++db) o[db] *= inv;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const u32x2 x0 = ds_read_tr16(smem + v_off(16 * ks, db));
-      const u32x2 x1 = ds_read_tr16(smem + v_off(16 * ks + 4, db));
-      o[db] = mfma32x32x16(u32x4{x0[0], x0[1], x1[0], x1[1]}, bq, o[db]);
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      // contraction slot 8*hh + e holds dk = 16*ks + 8*(e/4) + 4*hh + e%4
+      const u32x2 q0v = buf_load8(rqp, my_q * rsb + (ks * 16 + 4 * hh) * 2);
+      const u32x2 q1v = buf_load8(rqp, my_q * rsb + (ks * 16 + 8 + 4 * hh) * 2);
+      const u32x4 bq = u32x4{q0v[0], q0v[1], q1v[0], q1v[1]};
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (db * C::KSTEPS + ks) * 1024 + lane * 16);
+        o[db] = mfma32x32x16(a, bq, o[db]);
+      }
+    }
+  } else {
+    // all of a thread's loads are issued before the first conversion, so
+    // their latencies overlap instead of adding up
+    const float* Sp = states + (long long)(b * H + h) * stride_bh + (long long)n * stride_frame;
+    constexpr int NPER = D * D / 4 / NT;  // 16-byte pieces of S per thread
+    static_assert(NPER * NT * 4 == D * D, "S must split evenly over the threads");
+    f32x4 sx[NPER];
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) sx[i] = *reinterpret_cast<const f32x4*>(Sp + (tid + i * NT) * 4);
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int p = tid + i * NT;
+      const int dk = p / (D / 4), dv0 = (p % (D / 4)) * 4;
+      const int off = dk * (D * 2) + (((dv0 >> 3) ^ v_swz<NCH>(dk)) << 4) + (dv0 & 7) * 2;
+      *reinterpret_cast<u32x2*>(smem + off) = u32x2{pack_bf16x2(sx[i][0], sx[i][1]), pack_bf16x2(sx[i][2], sx[i][3])};
+    }
+    __syncthreads();
+    if (!wave_active) return;
+    const float inv = 1.f / sum_across_halves(l0 + l1);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) o[db] *= inv;
+    // same contraction order as the fragment path (slot 8*hh + e <-> dk =
+    // 16*ks + 8*(e/4) + 4*hh + e%4), so both paths give identical results:
+    // the two transposed reads take rows 16*ks + 4*hh + i/4 and those + 8
+    const int srow = 4 * hh + (gi >> 2);
+    auto s_off = [&](int row, int db) {
+      const int col = vcol + 32 * db;
+      return row * (D * 2) + (((col >> 3) ^ v_swz<NCH>(row)) << 4) + (col & 7) * 2;
+    };
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const u32x2 q0v = buf_load8(rqp, my_q * rsb + (ks * 16 + 4 * hh) * 2);
+      const u32x2 q1v = buf_load8(rqp, my_q * rsb + (ks * 16 + 8 + 4 * hh) * 2);
+      const u32x4 bq = u32x4{q0v[0], q0v[1], q1v[0], q1v[1]};
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const u32x2 x0 = ds_read_tr16(smem + s_off(16 * ks + srow, db));
+        const u32x2 x1 = ds_read_tr16(smem + s_off(16 * ks + 8 + srow, db));
+        o[db] = mfma32x32x16(u32x4{x0[0], x0[1], x1[0], x1[1]}, bq, o[db]);
+      }
     }
   }
   if (my_q < L) {
@@ -414,15 +459,17 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const void* qp,
                             const float* states, long long stride_bh, long long stride_frame,
-                            void* out, const Shape& s, float scale, hipStream_t st) {
+                            const void* sfrag, void* out, const Shape& s, float scale,
+                            hipStream_t st) {
   const int qtiles = (s.L + QPB - 1) / QPB;
   const long long items = (long long)s.B * s.H * s.F * qtiles;
   const int grid = (int)((items + 7) / 8 * 8);
   const float c2 = scale * kLog2e;
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                              (const uint16_t*)qp, states, stride_bh, stride_frame, (uint16_t*)out,
-                              s.H, s.T, s.L, s.F, qtiles, (int)items, c2);
+                              (const uint16_t*)qp, states, stride_bh, stride_frame,
+                              (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
+                              qtiles, (int)items, c2);
   };
   if (s.d == 128) args(attn_bf16_kernel<128>);
   else args(attn_bf16_kernel<64>);

@@ -96,6 +96,9 @@ __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds,
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 
 // Row-major [rows][D] bf16 tiles read with ds_read_tr16: 32 lanes (one 256-byte
 // LDS cycle) read 4 consecutive rows x 64 bytes; XOR-ing the 16-byte chunk index

@@ -10,7 +10,8 @@
 //                           readout has read S_0 before it is overwritten).
 //   update_state = 1, F>1 : gram, scan (writes S_{n-1} snapshots to the
 //                           workspace and S_F to `state`), then the readout
-//                           on the snapshots.
+//                           on the snapshots (bf16 readout fragments on the
+//                           bf16 path, fp32 row-major on the fp32 path).
 #include <math.h>
 #include <stdint.h>
 
@@ -58,18 +59,19 @@ ha_status launched(hipError_t e) { return e == hipSuccess ? HA_OK : HA_ERR_DEVIC
 
 ha_status run_readout(const void* q, const void* k, const void* v, const void* qp,
                       const float* states, long long sbh, long long sfr, void* out,
-                      const ha::Shape& s, int dtype, float scale, hipStream_t st) {
+                      const ha::Shape& s, int dtype, float scale, hipStream_t st,
+                      const void* sfrag = nullptr) {
   if (dtype == HA_BF16)
-    return launched(ha::launch_attn_bf16(q, k, v, qp, states, sbh, sfr, out, s, scale, st));
+    return launched(ha::launch_attn_bf16(q, k, v, qp, states, sbh, sfr, sfrag, out, s, scale, st));
   return launched(ha::launch_attn_fp32(q, k, v, qp, states, sbh, sfr, out, s, scale, st));
 }
 
 ha_status run_update(const void* kp, const void* vp, const float* alpha, const float* beta,
                      float* state, float* snaps, float* gram, const ha::Shape& s, int dtype,
-                     hipStream_t st) {
+                     hipStream_t st, void* sfrag = nullptr) {
   if (dtype == HA_BF16) {
     if (ha::launch_gram_bf16(kp, vp, beta, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
-    return launched(ha::launch_state_scan_bf16(gram, alpha, state, snaps, s, st));
+    return launched(ha::launch_state_scan_bf16(gram, alpha, state, snaps, sfrag, s, st));
   }
   if (ha::launch_gram_fp32(kp, vp, beta, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
   return launched(ha::launch_state_scan_fp32(gram, alpha, state, snaps, s, st));
@@ -191,7 +193,15 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
     if (r != HA_OK) return r;
     return run_update(kp, vp, alpha, beta, state, nullptr, gram, s, dtype, st);
   }
-  float* snaps = (float*)((char*)workspace + align_up(ha::gram_bytes(s)));
+  void* snap_area = (char*)workspace + align_up(ha::gram_bytes(s));
+  if (dtype == HA_BF16) {
+    // S_{n-1} of every frame as bf16 readout fragments (the readout rounds the
+    // state to bf16 either way)
+    r = run_update(kp, vp, alpha, beta, state, nullptr, gram, s, dtype, st, snap_area);
+    if (r != HA_OK) return r;
+    return run_readout(q, k, v, qp, nullptr, 0, 0, out, s, dtype, scale, st, snap_area);
+  }
+  float* snaps = (float*)snap_area;
   r = run_update(kp, vp, alpha, beta, state, snaps, gram, s, dtype, st);
   if (r != HA_OK) return r;
   return run_readout(q, k, v, qp, snaps, (long long)s.F * dd, dd, out, s, dtype, scale, st);

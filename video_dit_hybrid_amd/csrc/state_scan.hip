@@ -33,7 +33,8 @@ template <int D>
 __global__ __launch_bounds__(NTM) void state_scan_mfma_kernel(const unsigned char* __restrict__ ws,
                                                               const float* __restrict__ alpha,
                                                               float* __restrict__ state,
-                                                              float* __restrict__ snaps, int H,
+                                                              float* __restrict__ snaps,
+                                                              u32x4* __restrict__ sfrag, int H,
                                                               int F) {
   constexpr int NRB = D / 32;                       // 32-row bands (= waves in use)
   constexpr int NCB = D / CWM;
@@ -109,6 +110,8 @@ __global__ __launch_bounds__(NTM) void state_scan_mfma_kernel(const unsigned cha
         }
         lds[SL][0][2 * wave + sh][lane] = hi;
         lds[SL][1][2 * wave + sh][lane] = lo;
+        // bf16(S_{n-1}) for the readout: the same fragment, one 16-byte store
+        if (sfrag) sfrag[(((size_t)bh * F + n) * NCB + cb) * KS * 64 + (2 * wave + sh) * 64 + lane] = hi;
       }
     }
     lds_barrier();
@@ -202,14 +205,14 @@ __global__ __launch_bounds__(NT) void state_scan_fp32_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_state_scan_bf16(const void* ws, const float* alpha, float* state, float* snapshots,
-                                  const Shape& s, hipStream_t st) {
+                                  void* sfrag, const Shape& s, hipStream_t st) {
   const int groups = s.B * s.H * (s.d / CWM);
   if (s.d == 128)
     state_scan_mfma_kernel<128><<<groups, NTM, 0, st>>>((const unsigned char*)ws, alpha, state,
-                                                        snapshots, s.H, s.F);
+                                                        snapshots, (u32x4*)sfrag, s.H, s.F);
   else
     state_scan_mfma_kernel<64><<<groups, NTM, 0, st>>>((const unsigned char*)ws, alpha, state,
-                                                       snapshots, s.H, s.F);
+                                                       snapshots, (u32x4*)sfrag, s.H, s.F);
   return hipGetLastError();
 }
 
