@@ -19,17 +19,37 @@
 namespace ha {
 namespace {
 
+// global -> LDS copies issued from inline asm: the compiler cannot tell which
+// LDS buffer such a copy writes and would otherwise wait for every copy in
+// flight before each LDS read; completion is tracked by explicit vmcnt waits.
+// m0 holds the wave-uniform LDS destination.
+__device__ __forceinline__ void dma16_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bytes), (uint32_t)kRsrcWord3};
+}
+
 constexpr int TC = 64;   // tokens per LDS chunk
 constexpr int NW = 8;    // waves per work-group
 constexpr int NT = NW * kWave;
 
-// grid: one work-group per (b, h, frame). Waves 0-3 compute G = K'^T diag(beta)
-// K', waves 4-7 compute B = K'^T diag(beta) V', each wave a 32-row band of the
-// d x d result, contracting over the frame's tokens in chunks of 64.
+// grid: one work-group per (b, h, frame). Wave w owns the 32-row band
+// rb = w % (d/32) of both G = K'^T diag(beta) K' and B = K'^T diag(beta) V'
+// (the two share their A operand (beta K')^T), and the k-steps kh = w / (d/32)
+// of every 64-token chunk; the token halves are summed through LDS at the end.
 //
 // The K', V' chunks arrive row-major ([token][d] bf16, as stored) by direct
-// global -> LDS loads, two chunks in flight, and beta by a 4-byte-per-lane load;
-// tokens >= L are outside the buffer descriptors' range and arrive as zeros.
+// global -> LDS loads, three chunks in flight, and beta by a 4-byte-per-lane
+// load; tokens >= L are outside the buffer descriptors' range and arrive as zeros.
 // Both MFMA operands need 8 consecutive tokens per lane, which transposed LDS
 // reads deliver without any transposing write. The A operand beta*K' is formed
 // in fp32 in registers and split into bf16 hi + lo (two MFMAs), which keeps
@@ -49,10 +69,14 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   constexpr int SEGS = TILE / 1024;          // 1 KB direct-to-LDS segments per tile
   constexpr int RPS = 64 / NCH;              // rows per segment
   constexpr int NRB = D / 32;                // 32-row (and -column) blocks
-  constexpr int NB = NRB * NRB / 4;          // output blocks per wave
+  constexpr int KH = NW / NRB;               // waves sharing a row band (token split)
+  constexpr int KSC = TC / 16;               // k-steps per chunk
+  static_assert(KSC % KH == 0, "token split");
   static_assert(SEGS % NW == 0 || SEGS == NW, "segment split");
-  static_assert(NB == NRB || NB == 1, "a wave's blocks share one row band");
-  __shared__ __align__(16) unsigned char smem[2 * BUF];
+  constexpr int NBUF = 4;                    // chunks in flight
+  constexpr int PART = NRB * 2 * 16 * 64 * 4;  // one wave's partial sums (G and B blocks)
+  constexpr int SMEM = (KH - 1) * NRB * PART > NBUF * BUF ? (KH - 1) * NRB * PART : NBUF * BUF;
+  __shared__ __align__(16) unsigned char smem[SMEM];
 
   const int hf = blockIdx.x;
   const int h = hf % H;
@@ -60,18 +84,18 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   const int b = hf / (H * F);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31, hh = lane >> 5;
-  const int half = wave >> 2;                 // 0: G, 1: B
-  const int q0 = (wave & 3) * NB;             // first block index within the half
-  const int rb = q0 / NRB;                    // row band (shared by the wave's blocks)
+  const int hh = lane >> 5;
+  const int rb = wave % NRB;                 // row band of G and B
+  const int kh = wave / NRB;                 // which k-steps of each chunk
 
   const uint32_t rsb = (uint32_t)H * D * 2;
   const long long fbase = ((long long)b * T + (long long)n * L) * ((long long)H * D) + (long long)h * D;
   const int span = (int)((uint32_t)(L - 1) * rsb + D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + fbase, span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + fbase, span);
-  const __amdgpu_buffer_rsrc_t rbeta =
-      make_rsrc(beta + ((long long)b * T + (long long)n * L) * H + h, (int)(((uint32_t)(L - 1) * H + 1) * 4));
+  const u32x4 rk = rsrc_words(kp + fbase, span);
+  const u32x4 rv = rsrc_words(vp + fbase, span);
+  const u32x4 rbeta =
+      rsrc_words(beta + ((long long)b * T + (long long)n * L) * H + h, (int)(((uint32_t)(L - 1) * H + 1) * 4));
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(smem));
 
   // direct-to-LDS: wave w fills segments w, w + NW, ... of each tile; those are
   // NW*RPS rows apart, which leaves the transposed-read swizzle unchanged.
@@ -79,15 +103,15 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   const int srow = wave * RPS + lane / NCH, spc = lane % NCH;
   const uint32_t soff = srow * rsb + ((spc ^ tr_swz<NCH>(srow)) << 4);
   auto issue = [&](int c, int buf) {
-    unsigned char* base = smem + buf * BUF;
+    const uint32_t base = lds0 + buf * BUF;
     const uint32_t toff = (uint32_t)c * TC * rsb;
 #pragma unroll
     for (int i = 0; i < MY_SEGS; ++i) {
       const uint32_t so = toff + (uint32_t)i * NW * RPS * rsb;
-      dma16_to_lds(rk, base + (wave + NW * i) * 1024, soff, so);
-      dma16_to_lds(rv, base + TILE + (wave + NW * i) * 1024, soff, so);
+      dma16_asm(rk, base + (wave + NW * i) * 1024, soff, so);
+      dma16_asm(rv, base + TILE + (wave + NW * i) * 1024, soff, so);
     }
-    if (wave == 0) dma4_to_lds(rbeta, base + 2 * TILE, (uint32_t)lane * H * 4, (uint32_t)c * TC * H * 4);
+    if (wave == 0) dma4_asm(rbeta, base + 2 * TILE, (uint32_t)lane * H * 4, (uint32_t)c * TC * H * 4);
   };
 
   // transposed-read offsets: 16-lane group g reads rows 8*hh + gi/4 (+4) of a
@@ -106,23 +130,37 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
     return u32x4{x0[0], x0[1], x1[0], x1[1]};
   };
 
-  f32x16 acc[NB];
+  f32x16 ag[NRB], ab[NRB];  // G and B blocks (rb, cb) of this wave's tokens
 #pragma unroll
-  for (int i = 0; i < NB; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NRB; ++i) ag[i] = ab[i] = f32x16{};
 
   const int nch = (L + TC - 1) / TC;
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  for (int c = 0; c < NBUF - 1 && c < nch; ++c) issue(c, c);
   for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nch) issue(c + 1, buf ^ 1);
+    const int buf = c % NBUF;
+    // chunk c landed: at most the loads of the chunks after it are outstanding
+    const int later = (nch - 1 - c) < (NBUF - 2) ? (nch - 1 - c) : (NBUF - 2);
+    if (wave == 0) {
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (2 * MY_SEGS + 1)));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS + 1));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * 2 * MY_SEGS));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __syncthreads();
+    // the buffer of chunk c-1 is free (every wave passed the barrier above
+    // after consuming it): refill it with chunk c+NBUF-1
+    if (c + NBUF - 1 < nch) issue(c + NBUF - 1, (c + NBUF - 1) % NBUF);
     const unsigned char* kt = smem + buf * BUF;
-    const unsigned char* bt = half ? kt + TILE : kt;
+    const unsigned char* vt = kt + TILE;
     const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
 #pragma unroll
-    for (int ks = 0; ks < TC / 16; ++ks) {
-      // A = (beta K')^T rows 32*rb.., tokens 16*ks + 8*hh + e: split hi + lo
+    for (int kk = 0; kk < KSC / KH; ++kk) {
+      const int ks = kh * (KSC / KH) + kk;
+      // A = (beta K')^T rows 32*rb.., tokens 16*ks + 8*hh + e: split hi + lo,
+      // shared by the G blocks (B operand K') and the B blocks (B operand V')
       const u32x4 kraw = tr8(kt, ks, rb);
       const f32x4 b0 = *reinterpret_cast<const f32x4*>(be + 16 * ks + 8 * hh);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(be + 16 * ks + 8 * hh + 4);
@@ -138,14 +176,50 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
         alo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
       }
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const u32x4 bop = tr8(bt, ks, (q0 + i) % NRB);
-        acc[i] = mfma32x32x16(ahi, bop, acc[i]);
-        acc[i] = mfma32x32x16(alo, bop, acc[i]);
+      for (int cb = 0; cb < NRB; ++cb) {
+        const u32x4 bk = tr8(kt, ks, cb);
+        const u32x4 bv = tr8(vt, ks, cb);
+        ag[cb] = mfma32x32x16(ahi, bk, ag[cb]);
+        ab[cb] = mfma32x32x16(ahi, bv, ab[cb]);
+        ag[cb] = mfma32x32x16(alo, bk, ag[cb]);
+        ab[cb] = mfma32x32x16(alo, bv, ab[cb]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // sum the token halves: waves with kh > 0 hand their partial blocks to the
+  // kh = 0 wave of the same row band through LDS (lane-linear, conflict-free)
+  if constexpr (KH > 1) {
+    __syncthreads();  // every wave is done with the chunk buffers
+    f32x4* part = reinterpret_cast<f32x4*>(smem);
+    if (kh > 0) {
+      f32x4* my = part + ((size_t)((kh - 1) * NRB + rb) * NRB * 2 * 4) * 64;
+#pragma unroll
+      for (int cb = 0; cb < NRB; ++cb)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          my[((cb * 2 + 0) * 4 + v4) * 64 + lane] = f32x4{ag[cb][4 * v4], ag[cb][4 * v4 + 1], ag[cb][4 * v4 + 2], ag[cb][4 * v4 + 3]};
+          my[((cb * 2 + 1) * 4 + v4) * 64 + lane] = f32x4{ab[cb][4 * v4], ab[cb][4 * v4 + 1], ab[cb][4 * v4 + 2], ab[cb][4 * v4 + 3]};
+        }
+    }
     __syncthreads();
+    if (kh > 0) return;
+#pragma unroll
+    for (int j = 1; j < KH; ++j) {
+      const f32x4* src = part + ((size_t)((j - 1) * NRB + rb) * NRB * 2 * 4) * 64;
+#pragma unroll
+      for (int cb = 0; cb < NRB; ++cb)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 xg = src[((cb * 2 + 0) * 4 + v4) * 64 + lane];
+          const f32x4 xb = src[((cb * 2 + 1) * 4 + v4) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ag[cb][4 * v4 + e] += xg[e];
+            ab[cb][4 * v4 + e] += xb[e];
+          }
+        }
+    }
   }
 
   // Workspace per (b, h, frame), in the scan's MFMA fragment order:
@@ -163,28 +237,24 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   u32x4* glo = reinterpret_cast<u32x4*>(base + (size_t)D * D * 2);
   f32x4* bfr = reinterpret_cast<f32x4*>(base + (size_t)D * D * 4);
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int cb = (q0 + i) % NRB;
-    if (half) {
-      f32x4* dst = bfr + ((size_t)(cb * NRB + rb) * 64 + lane) * 4;
+  for (int cb = 0; cb < NRB; ++cb) {
+    f32x4* dst = bfr + ((size_t)(cb * NRB + rb) * 64 + lane) * 4;
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4)
-        dst[v4] = f32x4{acc[i][4 * v4], acc[i][4 * v4 + 1], acc[i][4 * v4 + 2], acc[i][4 * v4 + 3]};
-    } else {
+    for (int v4 = 0; v4 < 4; ++v4)
+      dst[v4] = f32x4{ab[cb][4 * v4], ab[cb][4 * v4 + 1], ab[cb][4 * v4 + 2], ab[cb][4 * v4 + 3]};
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        u32x4 hi, lo;
+    for (int sh = 0; sh < 2; ++sh) {
+      u32x4 hi, lo;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const float x0 = -acc[i][8 * sh + 2 * w2], x1 = -acc[i][8 * sh + 2 * w2 + 1];
-          const uint32_t hp = pack_bf16x2(x0, x1);
-          hi[w2] = hp;
-          lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
-        }
-        const size_t fo = (size_t)(cb * KS + 2 * rb + sh) * 64 + lane;
-        ghi[fo] = hi;
-        glo[fo] = lo;
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float x0 = -ag[cb][8 * sh + 2 * w2], x1 = -ag[cb][8 * sh + 2 * w2 + 1];
+        const uint32_t hp = pack_bf16x2(x0, x1);
+        hi[w2] = hp;
+        lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
       }
+      const size_t fo = (size_t)(cb * KS + 2 * rb + sh) * 64 + lane;
+      ghi[fo] = hi;
+      glo[fo] = lo;
     }
   }
 }
