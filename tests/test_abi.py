@@ -67,6 +67,7 @@ def fwd(**kw):
     (dict(kp=None), 1), (dict(alpha=None), 1), (dict(beta=None), 1),
     (dict(B=0), 2), (dict(H=-1), 2), (dict(T=0), 2), (dict(L=0), 2), (dict(T=65), 2),
     (dict(B=1 << 20, H=1 << 12, T=1 << 20, L=1), 2),
+    (dict(T=40000, L=1, d=128), 2),   # per-(stream, head) state increments past 32-bit offsets
     (dict(d=96), 3), (dict(d=256), 3), (dict(dtype=2), 3),
     (dict(q=4097), 4), (dict(out=(1 << 40) + 8), 4), (dict(alpha=28673), 4), (dict(state=36868), 4),
     (dict(ws=None), 5), (dict(ws_bytes=100), 5),

@@ -37,8 +37,10 @@ ha_status check_shape(int B, int H, int T, int d, int L, int dtype, ha::Shape* s
   const long long items = (long long)B * H * (T / L) * ((L + 63) / 64);
   if (items > kMaxItems) return HA_ERR_SHAPE;
   if ((long long)B * H * (T / L) * 2 > kMaxItems) return HA_ERR_SHAPE;
-  // one (stream, head, frame) slab is addressed with 32-bit byte offsets
+  // one (stream, head, frame) slab is addressed with 32-bit byte offsets, and
+  // so are the per-frame state increments of one (stream, head)
   if (((long long)L * H * d + d) * 4 > kMaxItems) return HA_ERR_SHAPE;
+  if ((long long)(T / L) * d * d * 8 > kMaxItems) return HA_ERR_SHAPE;
   *s = ha::Shape{B, H, T, d, L, T / L};
   return HA_OK;
 }

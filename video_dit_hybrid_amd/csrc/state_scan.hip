@@ -5,15 +5,16 @@
 // Column j of S_n depends only on column j of S_{n-1}, so a work-group owns a
 // column block of one (b, h) state and walks the frames in order.
 //
-// bf16 path (state_scan_mfma_kernel): the block is 32 columns; wave w keeps
-// rows [32w, 32w+32) of it in MFMA accumulators (fp32) for the whole walk.
-// Per step: S_{n-1} is split into bf16 hi + lo and shared through LDS as MFMA
-// B fragments (the accumulator layout already is one, in the contraction order
-// the gram kernel writes -G in); the accumulators are set to
+// bf16 path (state_scan_mfma_kernel): the block is 32 columns; compute wave w
+// keeps rows [32w, 32w+32) of it in MFMA accumulators (fp32) for the whole
+// walk. Per step: S_{n-1} is split into bf16 hi + lo and shared through LDS as
+// MFMA B fragments (the accumulator layout already is one, in the contraction
+// order the gram kernel writes -G in); the accumulators are set to
 // alpha S_{n-1} + B_n; then
 // acc += (-G)_hi S_hi + (-G)_hi S_lo + (-G)_lo S_hi on MFMA, which keeps the
-// product fp32-accurate (~16 mantissa bits per operand). The operands of step
-// n+2 (G rows, B block, alpha) are loaded while step n computes.
+// product fp32-accurate (~16 mantissa bits per operand). One more wave per
+// work-group copies -G of the frames ahead into LDS (two frames buffered), so
+// the compute waves never stall issuing those 64 KB per step.
 //
 // fp32 path (state_scan_fp32_kernel): the block is 16 columns in LDS and the
 // product is plain fp32 FMA, for callers whose inputs are fp32.
@@ -27,20 +28,31 @@ namespace {
 
 // ---------------------------------------------------------------- bf16 path
 constexpr int CWM = 32;   // state columns per work-group
-constexpr int NTM = 256;  // 4 waves, one 32-row block each (D = 128); D = 64 uses 2 waves
 
+// inline-asm global -> LDS copy (the compiler would otherwise order every
+// later LDS read behind it); completion is tracked by explicit vmcnt waits
+__device__ __forceinline__ void dma16_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
+}
+
+// Waves 0..NRB-1 compute (wave w: rows [32w, 32w+32) of the column block);
+// wave NRB only copies -G of the frames ahead into LDS, so the compute waves
+// never wait for those loads to issue. Two barriers per frame:
+//   E_n: the S_{n-1} fragments and -G_n are in LDS;
+//   F_n: the compute waves hold -G_n in registers (its buffer may be refilled).
 template <int D>
-__global__ __launch_bounds__(NTM) void state_scan_mfma_kernel(const unsigned char* __restrict__ ws,
-                                                              const float* __restrict__ alpha,
-                                                              float* __restrict__ state,
-                                                              float* __restrict__ snaps,
-                                                              u32x4* __restrict__ sfrag, int H,
-                                                              int F) {
-  constexpr int NRB = D / 32;                       // 32-row bands (= waves in use)
+__global__ __launch_bounds__((D / 32 + 1) * 64) void state_scan_mfma_kernel(
+    const unsigned char* __restrict__ ws, const float* __restrict__ alpha, float* __restrict__ state,
+    float* __restrict__ snaps, u32x4* __restrict__ sfrag, int H, int F) {
+  constexpr int NRB = D / 32;                       // 32-row bands (= compute waves)
   constexpr int NCB = D / CWM;
   constexpr int KS = D / 16;                        // k-steps over d_k
   constexpr size_t PER = (size_t)D * D * 8;         // workspace bytes per (b, h, frame)
-  // S operand fragments [k-step][lane] 16 bytes, hi and lo planes, double buffered
+  constexpr int GB = D * D * 4;                     // -G hi + lo bytes per frame
+  constexpr int NSEG = GB / 1024;                   // 1 KB copies per frame
+  // -G hi and lo fragments of two frames, then the S exchange (hi, lo; two frames)
+  __shared__ __align__(16) unsigned char gbuf[2][GB];
   __shared__ __align__(16) u32x4 lds[2][2][KS][64];
 
   const int cb = blockIdx.x % NCB;
@@ -49,100 +61,126 @@ __global__ __launch_bounds__(NTM) void state_scan_mfma_kernel(const unsigned cha
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
-  const bool active = wave < NRB;
-  const int row0 = wave * 32;
-  const int col = cb * CWM + lr;
 
-  // running state block in the 32x32 MFMA accumulator layout:
-  // acc[r] = S[row0 + 8*(r/4) + 4*hh + r%4][col]
-  f32x16 acc = f32x16{};
-  float* sbase = state + (size_t)bh * D * D;
-  if (active) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col];
+  if (wave == NRB) {
+    // ---- loader: -G_n of frame n into gbuf[n % 2], lane-linear (fragment order kept)
+    const unsigned char* wsb = ws + (size_t)bh * F * PER;
+    const uint64_t a = (uint64_t)wsb;
+    const u32x4 rs = u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)),
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((size_t)F * PER)),
+                           (uint32_t)kRsrcWord3};
+    const uint32_t lds_g = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(&gbuf[0][0]));
+    auto load = [&](int n) {
+#pragma unroll 8
+      for (int i = 0; i < NSEG; ++i)
+        dma16_asm(rs, lds_g + (n & 1) * GB + i * 1024, lane * 16, (uint32_t)((size_t)n * PER) + i * 1024);
+    };
+    // s_waitcnt immediate for "at most N vector-memory operations outstanding"
+    // (vmcnt is 6 bits: N is capped at 63; expcnt and lgkmcnt left at their maxima)
+    constexpr int NW_ = NSEG < 63 ? NSEG : 63;
+    constexpr int kWaitNewOnly = (NW_ & 0xF) | (0x7 << 4) | (0xF << 8) | (((NW_ >> 4) & 3) << 14);
+    load(0);
+    if (F > 1) load(1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // -G_0 and -G_1 in LDS
+    for (int n = 0; n < F; ++n) {
+      lds_barrier();  // E_n
+      lds_barrier();  // F_n
+      // -G_{n+2} into the buffer -G_n leaves; -G_{n+1} (issued earlier) must
+      // have landed before E_{n+1}: wait until only the new copies (or fewer) remain
+      if (n + 2 < F) {
+        load(n + 2);
+        __builtin_amdgcn_s_waitcnt(kWaitNewOnly);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+    }
+    return;
   }
 
-  // operands of one step (-G hi and lo A fragments of this band, the B block,
-  // alpha) in a two-slot ring: step n's operands are requested two steps
-  // earlier. Each request is one contiguous 1 KB per wave (fragment order).
-  u32x4 gh[2][KS], gl[2][KS];
+  // ---- compute waves
+  const int row0 = wave * 32;
+  const int col = cb * CWM + lr;
+  f32x16 acc = f32x16{};
+  float* sbase = state + (size_t)bh * D * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col];
+
+  // B block and alpha of a frame, two frames ahead (registers)
   f32x4 bv[2][4];
   float al[2] = {0.f, 0.f};
   auto fetch = [&](int slot, int n) {
     const unsigned char* base = ws + ((size_t)bh * F + n) * PER;
-    const u32x4* ghp = reinterpret_cast<const u32x4*>(base) + (size_t)wave * KS * 64 + lane;
-    const u32x4* glp = reinterpret_cast<const u32x4*>(base + (size_t)D * D * 2) + (size_t)wave * KS * 64 + lane;
     const f32x4* bp = reinterpret_cast<const f32x4*>(base + (size_t)D * D * 4) + ((size_t)(cb * NRB + wave) * 64 + lane) * 4;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      gh[slot][ks] = ghp[ks * 64];
-      gl[slot][ks] = glp[ks * 64];
-    }
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) bv[slot][v4] = bp[v4];
     al[slot] = alpha[((size_t)b * F + n) * H + h];
   };
-  if (active) {
-    fetch(0, 0);
-    if (F > 1) fetch(1, 1);
-  }
+  fetch(0, 0);
+  if (F > 1) fetch(1, 1);
 
-  // one frame; slot == n % 2 (also the LDS buffer), fixed at compile time
+  // S_{n-1} -> exchange buffer SL as B fragments (k-steps 2*wave, 2*wave+1 of
+  // this band: registers [8s, 8s+8)), plus the snapshots of frame n
+  auto publish = [&](auto slot_c, int n) {
+    constexpr int SL = decltype(slot_c)::value;
+    if (snaps) {
+      float* dst = snaps + ((size_t)bh * F + n) * D * D;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
+    }
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float x0 = acc[8 * sh + 2 * w2], x1 = acc[8 * sh + 2 * w2 + 1];
+        const uint32_t hp = pack_bf16x2(x0, x1);
+        hi[w2] = hp;
+        lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
+      }
+      lds[SL][0][2 * wave + sh][lane] = hi;
+      lds[SL][1][2 * wave + sh][lane] = lo;
+      if (sfrag) sfrag[(((size_t)bh * F + n) * NCB + cb) * KS * 64 + (2 * wave + sh) * 64 + lane] = hi;
+    }
+  };
+
   auto step = [&](auto slot_c, int n) {
     constexpr int SL = decltype(slot_c)::value;
-    if (active) {
-      if (snaps) {  // S_{n-1}, the state frame n's readout reads
-        float* dst = snaps + ((size_t)bh * F + n) * D * D;
+    lds_barrier();  // E_n
+    u32x4 gh[KS], gl[KS];
+    const u32x4* gp = reinterpret_cast<const u32x4*>(&gbuf[SL][0]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
-      }
-      // this band's rows of S_{n-1} are the B fragments of k-steps 2*wave, 2*wave+1
-      // (same contraction order as the -G fragments): registers [8s, 8s+8)
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        u32x4 hi, lo;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const float x0 = acc[8 * sh + 2 * w2], x1 = acc[8 * sh + 2 * w2 + 1];
-          const uint32_t hp = pack_bf16x2(x0, x1);
-          hi[w2] = hp;
-          lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
-        }
-        lds[SL][0][2 * wave + sh][lane] = hi;
-        lds[SL][1][2 * wave + sh][lane] = lo;
-        // bf16(S_{n-1}) for the readout: the same fragment, one 16-byte store
-        if (sfrag) sfrag[(((size_t)bh * F + n) * NCB + cb) * KS * 64 + (2 * wave + sh) * 64 + lane] = hi;
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      gh[ks] = gp[(wave * KS + ks) * 64 + lane];
+      gl[ks] = gp[(NRB * KS + wave * KS + ks) * 64 + lane];
     }
-    lds_barrier();
-    if (active) {
-      f32x16 nacc;
+    lds_barrier();  // F_n (waits for the reads above)
+    f32x16 nacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) nacc[r] = fmaf(al[SL], acc[r], bv[SL][r >> 2][r & 3]);
+    for (int r = 0; r < 16; ++r) nacc[r] = fmaf(al[SL], acc[r], bv[SL][r >> 2][r & 3]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 shi = lds[SL][0][ks][lane];
-        const u32x4 slo = lds[SL][1][ks][lane];
-        nacc = mfma32x32x16(gh[SL][ks], shi, nacc);
-        nacc = mfma32x32x16(gh[SL][ks], slo, nacc);
-        nacc = mfma32x32x16(gl[SL][ks], shi, nacc);
-      }
-      if (n + 2 < F) fetch(SL, n + 2);
-      acc = nacc;
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 shi = lds[SL][0][ks][lane];
+      const u32x4 slo = lds[SL][1][ks][lane];
+      nacc = mfma32x32x16(gh[ks], shi, nacc);
+      nacc = mfma32x32x16(gh[ks], slo, nacc);
+      nacc = mfma32x32x16(gl[ks], shi, nacc);
     }
+    if (n + 2 < F) fetch(SL, n + 2);
+    acc = nacc;
+    if (n + 1 < F) publish(std::integral_constant<int, SL ^ 1>{}, n + 1);
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  publish(S0{}, 0);
   int n = 0;
   for (; n + 1 < F; n += 2) {
     step(S0{}, n);
     step(S1{}, n + 1);
   }
   if (n < F) step(S0{}, n);
-  if (active) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
-  }
+  for (int r = 0; r < 16; ++r) sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -208,11 +246,11 @@ hipError_t launch_state_scan_bf16(const void* ws, const float* alpha, float* sta
                                   void* sfrag, const Shape& s, hipStream_t st) {
   const int groups = s.B * s.H * (s.d / CWM);
   if (s.d == 128)
-    state_scan_mfma_kernel<128><<<groups, NTM, 0, st>>>((const unsigned char*)ws, alpha, state,
-                                                        snapshots, (u32x4*)sfrag, s.H, s.F);
+    state_scan_mfma_kernel<128><<<groups, (128 / 32 + 1) * 64, 0, st>>>(
+        (const unsigned char*)ws, alpha, state, snapshots, (u32x4*)sfrag, s.H, s.F);
   else
-    state_scan_mfma_kernel<64><<<groups, NTM, 0, st>>>((const unsigned char*)ws, alpha, state,
-                                                       snapshots, (u32x4*)sfrag, s.H, s.F);
+    state_scan_mfma_kernel<64><<<groups, (64 / 32 + 1) * 64, 0, st>>>(
+        (const unsigned char*)ws, alpha, state, snapshots, (u32x4*)sfrag, s.H, s.F);
   return hipGetLastError();
 }
 
