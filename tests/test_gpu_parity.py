@@ -350,3 +350,53 @@ def test_long_stream_constant_memory_and_parity():
                     worst_o = max(worst_o, rel_err(W.to_f64(o[0, :, h], "bf16"), ref))
     say(f"stream: rel_err state {worst_s:.3e} after 120 frames (all heads), out {worst_o:.3e}")
     assert worst_s < TOL_STATE and worst_o < TOL_OUT
+
+
+def test_graph_replay_matches_eager():
+    # One frame of a streaming run (a denoise call, then the clean call) captured
+    # in a HIP graph and replayed: every replay must equal the eager calls
+    # bitwise, with eager work and synchronisations between the replays.
+    w = small("stream", H=2, L=200, frames=1)
+    say("case graph replay")
+    d_in = upload(W.make_call_inputs(w, 0, 1, 0, clean=False), "bf16")
+    c_in = upload(W.make_call_inputs(w, 0, 1, w.denoise_passes, clean=True), "bf16")
+    s0 = torch.from_numpy(W.make_state0(w)).cuda()
+    out_d = torch.empty_like(d_in["q"])
+    out_c = torch.empty_like(c_in["q"])
+    ws = torch.empty(api.workspace_bytes(1, w.H, w.L, w.L, w.d, 1), dtype=torch.uint8, device="cuda")
+
+    def frame(state):
+        api.hybrid_attn_forward(d_in["q"], d_in["k"], d_in["v"], d_in["qp"], None, None, None, None,
+                                state, w.L, 0, out=out_d)
+        api.hybrid_attn_forward(c_in["q"], c_in["k"], c_in["v"], c_in["qp"], c_in["kp"], c_in["vp"],
+                                c_in["alpha"], c_in["beta"], state, w.L, 1, out=out_c, workspace=ws)
+
+    # eager reference for three frames
+    st = s0.clone()
+    ref = []
+    for _ in range(3):
+        frame(st)
+        torch.cuda.synchronize()
+        ref.append((out_d.clone(), out_c.clone(), st.clone()))
+    # graph of one frame on its own state tensor
+    gst = s0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        frame(gst)          # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gst.copy_(s0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        frame(gst)
+    torch.cuda.synchronize()
+    gst.copy_(s0)           # capture does not run the kernels; start from S_0
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_d, ref[i][0]) and torch.equal(out_c, ref[i][1])
+        assert torch.equal(gst, ref[i][2])
+        junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
