@@ -142,7 +142,7 @@ def bench_streaming(w, args):
         for p, t in enumerate(passes):
             if p < w.denoise_passes:
                 api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], None, None, None, None,
-                                        state, w.L, 0, out=out)
+                                        state, w.L, 0, out=out, workspace=ws)
             else:
                 api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], t["kp"], t["vp"], t["alpha"],
                                         t["beta"], state, w.L, 1, out=out, workspace=ws)

@@ -367,7 +367,7 @@ def test_graph_replay_matches_eager():
 
     def frame(state):
         api.hybrid_attn_forward(d_in["q"], d_in["k"], d_in["v"], d_in["qp"], None, None, None, None,
-                                state, w.L, 0, out=out_d)
+                                state, w.L, 0, out=out_d, workspace=ws)
         api.hybrid_attn_forward(c_in["q"], c_in["k"], c_in["v"], c_in["qp"], c_in["kp"], c_in["vp"],
                                 c_in["alpha"], c_in["beta"], state, w.L, 1, out=out_c, workspace=ws)
 
