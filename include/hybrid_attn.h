@@ -63,7 +63,11 @@ typedef enum {
  * Bytes of workspace hybrid_attn_forward needs for these sizes: 0 when
  * update_state is 0; otherwise the per-frame state increments (d x 2d fp32 per
  * stream, head and frame) plus, when T / frame_len > 1, the per-frame
- * pre-update states S_{N-1} (d x d fp32 each). Returns 0 for invalid sizes.
+ * pre-update states S_{N-1} (d x d fp32 each). A call with fewer than 128
+ * (stream, head, frame) groups computes each frame's increments in
+ * n = min(ceil(256 / groups), 16, ceil(frame_len / 64)) token splits and needs n
+ * more d x 2d fp32 blocks per group for their partial sums. The size depends on
+ * the arguments only. Returns 0 for invalid sizes.
  */
 size_t hybrid_attn_workspace_bytes(int B, int H, int T, int frame_len, int d,
                                    int update_state);
@@ -111,7 +115,8 @@ ha_status hybrid_attn_intra_readout(const void* q, const void* k,
 
 /*
  * Bytes of workspace hybrid_attn_state_update needs: the per-frame state
- * increments, B*H*F*d*2d fp32. Returns 0 for invalid sizes.
+ * increments, B*H*F*d*2d fp32, plus the token-split partial sums under the
+ * same rule as hybrid_attn_workspace_bytes. Returns 0 for invalid sizes.
  */
 size_t hybrid_attn_state_workspace_bytes(int B, int H, int T, int frame_len,
                                          int d);

@@ -44,7 +44,15 @@ def test_workspace_sizes():
     up = lambda x: (x + 255) // 256 * 256
     assert api.workspace_bytes(1, H, F * L, L, d, 0) == 0
     assert api.workspace_bytes(1, H, F * L, L, d, 1) == up(gram) + up(snaps)
-    assert api.workspace_bytes(1, H, L, L, d, 1) == up(H * d * 2 * d * 4)     # F = 1: no snapshots
+    # F = 1: no snapshots; only 12 (stream, head, frame) groups, so the
+    # increments are computed in min(ceil(256 / 12), 16, 25 chunks) = 16 token
+    # splits whose fp32 partial sums (d x 2d each) follow the increments
+    assert api.workspace_bytes(1, H, L, L, d, 1) == up(H * d * 2 * d * 4 * (1 + 16))
+    # 96 groups: 3 splits; 128 or more groups: no split
+    assert api.workspace_bytes(8, H, L, L, d, 1) == up(8 * H * d * 2 * d * 4 * (1 + 3))
+    assert api.workspace_bytes(1, 128, L, L, d, 1) == up(128 * d * 2 * d * 4)
+    # never more splits than 64-token chunks: L = 100 has 2
+    assert api.workspace_bytes(1, 1, 100, 100, d, 1) == up(d * 2 * d * 4 * (1 + 2))
     assert api.state_workspace_bytes(1, H, F * L, L, d) == up(gram)
     assert api.workspace_bytes(1, H, F * L + 1, L, d, 1) == 0                # invalid sizes
 

@@ -44,8 +44,31 @@ hipError_t launch_state_scan_bf16(const void* ws, const float* alpha, float* sta
 hipError_t launch_state_scan_fp32(const float* gram, const float* alpha, float* state,
                                   float* snapshots, const Shape& s, hipStream_t st);
 
-inline size_t gram_bytes(const Shape& s) {
+// Token splits of the state-increment (gram) pass: one work-group per
+// (stream, head, frame) leaves most of the GPU idle when there are few frames
+// (one frame per call while streaming), so those calls split each frame's
+// tokens over several work-groups, whose fp32 partial sums are added in split
+// order by a second pass. The count depends on the shape only, so equal shapes
+// always take the same path and give bitwise equal results.
+constexpr int kGramTargetGroups = 256;  // about one work-group per CU
+constexpr int kGramMaxSplits = 16;
+inline int gram_splits(const Shape& s) {
+  const long long groups = (long long)s.B * s.H * s.F;
+  if (groups * 2 >= kGramTargetGroups) return 1;
+  const int chunks = (s.L + 63) / 64;  // 64-token chunks per frame
+  int n = (int)((kGramTargetGroups + groups - 1) / groups);
+  if (n > kGramMaxSplits) n = kGramMaxSplits;
+  if (n > chunks) n = chunks;
+  return n < 1 ? 1 : n;
+}
+// per (stream, head, frame): the increments in the scan's format (d x 2d fp32
+// worth of bytes), then, when split, one d x 2d fp32 partial sum per split
+inline size_t gram_final_bytes(const Shape& s) {
   return (size_t)s.B * s.H * s.F * (size_t)s.d * 2 * s.d * sizeof(float);
+}
+inline size_t gram_bytes(const Shape& s) {
+  const int n = gram_splits(s);
+  return gram_final_bytes(s) * (n > 1 ? 1 + n : 1);
 }
 inline size_t snapshot_frag_bytes(const Shape& s) {
   return (size_t)s.B * s.H * s.F * (size_t)s.d * s.d * 2;

@@ -56,13 +56,57 @@ constexpr int NT = NW * kWave;
 // ~16 mantissa bits; K' and V' themselves are exact in bf16.
 //
 // Output, per (b, h, frame): -G as bf16 hi + lo and B as fp32, laid out in the
-// scan's MFMA fragment order (see the stores at the end).
+// scan's MFMA fragment order (store_increments). With nsplit > 1 the
+// work-group (b, h, frame, split) covers only its share of the 64-token chunks
+// and writes its fp32 partial sums instead (store_partial), which
+// gram_reduce_kernel adds up in split order.
+
+// Workspace per (b, h, frame), in the scan's MFMA fragment order:
+//   G hi : [band i (NRB)][k-step (D/16)][lane] 16 bytes  (8 bf16 of -G)
+//   G lo : the same for the low halves
+//   B    : [col block (NRB)][row band (NRB)][lane] 64 bytes (16 fp32)
+// G is symmetric, so the accumulator registers [8s, 8s+8) of the block
+// (row band kb, column block rb) are the scan's A fragment of -G for output
+// band rb and k-step 2*kb + s, under the contraction order in which k-slot
+// 8*hh + e of that step is k = 32*kb + 16*s + 8*(e/4) + 4*hh + e%4.
+// g8: accumulator elements [8*sh, 8*sh + 8) of the G block (row band rb,
+// column block cb) of one lane; -G is split into bf16 hi + lo.
+template <int D>
+__device__ __forceinline__ void store_g_half(unsigned char* base, int rb, int cb, int sh, int lane,
+                                             const float* g8) {
+  constexpr int KS = D / 16;
+  u32x4 hi, lo;
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const float x0 = -g8[2 * w2], x1 = -g8[2 * w2 + 1];
+    const uint32_t hp = pack_bf16x2(x0, x1);
+    hi[w2] = hp;
+    lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
+  }
+  const size_t fo = (size_t)(cb * KS + 2 * rb + sh) * 64 + lane;
+  reinterpret_cast<u32x4*>(base)[fo] = hi;
+  reinterpret_cast<u32x4*>(base + (size_t)D * D * 2)[fo] = lo;
+}
+// B block (row band rb, column block cb): accumulator elements [4*v4, 4*v4+4)
+template <int D>
+__device__ __forceinline__ void store_b4(unsigned char* base, int rb, int cb, int v4, int lane, f32x4 x) {
+  constexpr int NRB = D / 32;
+  reinterpret_cast<f32x4*>(base + (size_t)D * D * 4)[((size_t)(cb * NRB + rb) * 64 + lane) * 4 + v4] = x;
+}
+// fp32 partial sums of one split: [row band][col block][G, B][v4][lane] f32x4
+template <int D>
+__device__ __forceinline__ f32x4* partial_block(float* partial, size_t group_split, int rb, int cb) {
+  constexpr int NRB = D / 32;
+  return reinterpret_cast<f32x4*>(partial) + ((group_split * NRB + rb) * NRB + cb) * 2 * 4 * 64;
+}
+
 template <int D>
 __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restrict__ kp,
                                                        const uint16_t* __restrict__ vp,
                                                        const float* __restrict__ beta,
-                                                       float* __restrict__ gram, int H, int T, int L,
-                                                       int F) {
+                                                       float* __restrict__ gram,
+                                                       float* __restrict__ partial, int nsplit,
+                                                       int H, int T, int L, int F) {
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = TC * D * 2;           // bytes of one K' or V' chunk
   constexpr int BUF = 2 * TILE + TC * 4;     // K', V', beta
@@ -78,7 +122,7 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   constexpr int SMEM = (KH - 1) * NRB * PART > NBUF * BUF ? (KH - 1) * NRB * PART : NBUF * BUF;
   __shared__ __align__(16) unsigned char smem[SMEM];
 
-  const int hf = blockIdx.x;
+  const int hf = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
   const int h = hf % H;
   const int n = (hf / H) % F;
   const int b = hf / (H * F);
@@ -134,8 +178,11 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
 #pragma unroll
   for (int i = 0; i < NRB; ++i) ag[i] = ab[i] = f32x16{};
 
-  const int nch = (L + TC - 1) / TC;
-  for (int c = 0; c < NBUF - 1 && c < nch; ++c) issue(c, c);
+  // this split's chunks: [c0, c0 + nch) of the frame's chunks
+  const int nch_all = (L + TC - 1) / TC;
+  const int c0 = (int)((long long)sp * nch_all / nsplit);
+  const int nch = (int)((long long)(sp + 1) * nch_all / nsplit) - c0;
+  for (int c = 0; c < NBUF - 1 && c < nch; ++c) issue(c0 + c, c);
   for (int c = 0; c < nch; ++c) {
     const int buf = c % NBUF;
     // chunk c landed: at most the loads of the chunks after it are outstanding
@@ -152,7 +199,7 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
     __syncthreads();
     // the buffer of chunk c-1 is free (every wave passed the barrier above
     // after consuming it): refill it with chunk c+NBUF-1
-    if (c + NBUF - 1 < nch) issue(c + NBUF - 1, (c + NBUF - 1) % NBUF);
+    if (c + NBUF - 1 < nch) issue(c0 + c + NBUF - 1, (c + NBUF - 1) % NBUF);
     const unsigned char* kt = smem + buf * BUF;
     const unsigned char* vt = kt + TILE;
     const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
@@ -222,40 +269,67 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
     }
   }
 
-  // Workspace per (b, h, frame), in the scan's MFMA fragment order:
-  //   G hi : [band i (NRB)][k-step (D/16)][lane] 16 bytes  (8 bf16 of -G)
-  //   G lo : the same for the low halves
-  //   B    : [col block (NRB)][row band (NRB)][lane] 64 bytes (16 fp32)
-  // G is symmetric, so the accumulator registers [8s, 8s+8) of the block
-  // (row band kb, column block rb) are the scan's A fragment of -G for output
-  // band rb and k-step 2*kb + s, under the contraction order in which k-slot
-  // 8*hh + e of that step is k = 32*kb + 16*s + 8*(e/4) + 4*hh + e%4.
+  if (nsplit > 1) {
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) {
+      f32x4* dst = partial_block<D>(partial, (size_t)hf * nsplit + sp, rb, cb);
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        dst[(0 * 4 + v4) * 64 + lane] = f32x4{ag[cb][4 * v4], ag[cb][4 * v4 + 1], ag[cb][4 * v4 + 2], ag[cb][4 * v4 + 3]};
+        dst[(1 * 4 + v4) * 64 + lane] = f32x4{ab[cb][4 * v4], ab[cb][4 * v4 + 1], ab[cb][4 * v4 + 2], ab[cb][4 * v4 + 3]};
+      }
+    }
+    return;
+  }
+  // workspace order [b][h][frame] (the grid runs heads fastest)
   unsigned char* base = reinterpret_cast<unsigned char*>(gram) +
                         ((size_t)(b * H + h) * F + n) * (size_t)D * D * 8;
-  constexpr int KS = D / 16;
-  u32x4* ghi = reinterpret_cast<u32x4*>(base);
-  u32x4* glo = reinterpret_cast<u32x4*>(base + (size_t)D * D * 2);
-  f32x4* bfr = reinterpret_cast<f32x4*>(base + (size_t)D * D * 4);
 #pragma unroll
   for (int cb = 0; cb < NRB; ++cb) {
-    f32x4* dst = bfr + ((size_t)(cb * NRB + rb) * 64 + lane) * 4;
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4)
-      dst[v4] = f32x4{ab[cb][4 * v4], ab[cb][4 * v4 + 1], ab[cb][4 * v4 + 2], ab[cb][4 * v4 + 3]};
+      store_b4<D>(base, rb, cb, v4, lane, f32x4{ab[cb][4 * v4], ab[cb][4 * v4 + 1], ab[cb][4 * v4 + 2], ab[cb][4 * v4 + 3]});
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
-      u32x4 hi, lo;
+      float g8[8];
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const float x0 = -ag[cb][8 * sh + 2 * w2], x1 = -ag[cb][8 * sh + 2 * w2 + 1];
-        const uint32_t hp = pack_bf16x2(x0, x1);
-        hi[w2] = hp;
-        lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
-      }
-      const size_t fo = (size_t)(cb * KS + 2 * rb + sh) * 64 + lane;
-      ghi[fo] = hi;
-      glo[fo] = lo;
+      for (int e = 0; e < 8; ++e) g8[e] = ag[cb][8 * sh + e];
+      store_g_half<D>(base, rb, cb, sh, lane, g8);
     }
+  }
+}
+
+// Sum of the nsplit partial increments of one (b, h, frame), in split order,
+// stored in the scan's format. Work-group (hf, rb, cb) with hf the gram grid's
+// (b, frame, head) index, 256 threads: thread
+// part p = tid / 64 handles, for lane tid % 64, the G accumulator elements
+// [8p, 8p + 8) (p < 2) or the B elements [8(p-2), 8(p-2) + 8) (p >= 2).
+template <int D>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ partial,
+                                                          float* __restrict__ gram, int nsplit,
+                                                          int H, int F) {
+  constexpr int NRB = D / 32;
+  const int blk = blockIdx.x;
+  const int cb = blk % NRB, rb = (blk / NRB) % NRB;
+  const int hf = blk / (NRB * NRB);
+  const int h = hf % H, n = (hf / H) % F, b = hf / (H * F);
+  const int lane = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int gb = p >> 1, v0 = 2 * (p & 1);  // G or B, first of two 4-element pieces
+  f32x4 s0 = f32x4{}, s1 = f32x4{};
+#pragma unroll 8
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const f32x4* src = partial_block<D>(const_cast<float*>(partial), (size_t)hf * nsplit + sp, rb, cb);
+    s0 += src[(gb * 4 + v0) * 64 + lane];
+    s1 += src[(gb * 4 + v0 + 1) * 64 + lane];
+  }
+  unsigned char* base = reinterpret_cast<unsigned char*>(gram) +
+                        ((size_t)(b * H + h) * F + n) * (size_t)D * D * 8;
+  if (gb == 0) {
+    const float g8[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    store_g_half<D>(base, rb, cb, p & 1, lane, g8);
+  } else {
+    store_b4<D>(base, rb, cb, v0, lane, s0);
+    store_b4<D>(base, rb, cb, v0 + 1, lane, s1);
   }
 }
 
@@ -264,12 +338,17 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
 hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, float* gram,
                             const Shape& s, hipStream_t st) {
   const long long groups = (long long)s.B * s.H * s.F;
-  if (s.d == 128)
-    gram_bf16_kernel<128><<<(int)groups, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta,
-                                                      gram, s.H, s.T, s.L, s.F);
-  else
-    gram_bf16_kernel<64><<<(int)groups, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta,
-                                                     gram, s.H, s.T, s.L, s.F);
+  const int nsplit = gram_splits(s);
+  // partial sums after the increments (gram_bytes reserves both)
+  float* partial = nsplit > 1 ? gram + gram_final_bytes(s) / sizeof(float) : nullptr;
+  const int grid = (int)(groups * nsplit);
+  auto run = [&](auto gk, auto rk, int nrb) {
+    gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, gram, partial, nsplit, s.H,
+                            s.T, s.L, s.F);
+    if (nsplit > 1) rk<<<(int)(groups * nrb * nrb), 256, 0, st>>>(partial, gram, nsplit, s.H, s.F);
+  };
+  if (s.d == 128) run(gram_bf16_kernel<128>, gram_reduce_kernel<128>, 4);
+  else run(gram_bf16_kernel<64>, gram_reduce_kernel<64>, 2);
   return hipGetLastError();
 }
 
