@@ -29,6 +29,9 @@ Readings where the page is silent or garbled (each is listed in the design doc):
   * the branches combine by a plain sum, O = O_intra + O_inter;
   * the softmax scale is 1/sqrt(d) unless given; no mask inside a frame;
   * with update_state = 0 every frame reads the input state.
+  * the feature maps phi_q, phi_k, phi_v (2.1, "adaptation": grouped per-head
+    1x1 maps) are one d x d linear map per head, no bias, no nonlinearity,
+    applied to the inter-frame branch's inputs only.
 
 Every function here is pinned by tests/test_oracle_pins.py against
 properties the page and the mathematics fix (row sums, closed forms, the
@@ -142,3 +145,32 @@ def state_chain(kp, vp, alpha, beta, state, frame_len):
         S = delta_update(S, kp[r], vp[r], float(alpha[n]), beta[r])
         chain.append(S)
     return chain
+
+
+def feature_maps(q, k, v, wq, wk, wv):
+    """The grouped per-head 1x1 feature maps of the inter-frame branch
+    (ARL2 2.1, "adaptation": phi_q, phi_k, phi_v adapt the frozen projections'
+    Q, K, V to the linear recurrence). Read here as one d x d linear map per
+    head over that head's channels, no bias and no nonlinearity (a 1x1
+    convolution grouped by head):
+        Q'[b, t, h, :] = Q[b, t, h, :] @ wq[h]   (likewise K' with wk, V' with wv)
+    q, k, v: [B, T, H, d] fp64; wq, wk, wv: [H, d, d] fp64.
+    Returns (qp, kp, vp), each [B, T, H, d].
+    """
+    maps = []
+    for x, w in ((q, wq), (k, wk), (v, wv)):
+        y = np.empty_like(x, dtype=np.float64)
+        for h in range(x.shape[2]):
+            y[:, :, h, :] = x[:, :, h, :] @ w[h]
+        maps.append(y)
+    return tuple(maps)
+
+
+def hybrid_layer_fmap(q, k, v, wq, wk, wv, alpha, beta, state, frame_len,
+                      update_state, scale=None):
+    """The layer with the feature maps applied in front of the inter-frame
+    branch (ARL2 2.1): Q', K', V' = phi(Q, K, V), then hybrid_layer. The
+    intra-frame branch keeps the unmapped Q, K, V (2.1 item 1: the frozen
+    projections). Returns (out, state_out) as hybrid_layer."""
+    qp, kp, vp = feature_maps(q, k, v, wq, wk, wv)
+    return hybrid_layer(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale)

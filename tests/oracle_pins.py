@@ -288,7 +288,92 @@ def check_state_chain_matches_layer(o):
         assert np.max(np.abs(ch[-1] - S[0, h])) < 1e-14
 
 
+def _fmap_inputs(rng, B=1, T=8, H=3, d=4, L=4):
+    q, k, v, _, _, _, a, b, S0 = _inputs(rng, B=B, T=T, H=H, d=d, L=L)
+    w = [rng.standard_normal((H, d, d)) / math.sqrt(d) for _ in range(3)]
+    return q, k, v, w, a, b, S0
+
+
+def check_fmap_brute_force(o):
+    """Feature maps by scalar loops: Q'[b,t,h,e] = sum_j Q[b,t,h,j] W[h][j,e]
+    (a 1x1 map per head, grouped by head), then the layer on them."""
+    rng = np.random.default_rng(21)
+    q, k, v, (wq, wk, wv), a, b, S0 = _fmap_inputs(rng, B=2, T=8, H=2, d=3)
+    B, T, H, d = q.shape
+    maps = []
+    for x, w in ((q, wq), (k, wk), (v, wv)):
+        y = np.zeros_like(x)
+        for bb in range(B):
+            for t in range(T):
+                for h in range(H):
+                    for e in range(d):
+                        acc = 0.0
+                        for j in range(d):
+                            acc += x[bb, t, h, j] * w[h][j, e]
+                        y[bb, t, h, e] = acc
+        maps.append(y)
+    got = o.feature_maps(q, k, v, wq, wk, wv)
+    for g, want in zip(got, maps):
+        assert np.allclose(g, want, rtol=1e-12, atol=1e-12)
+    out, st = o.hybrid_layer_fmap(q, k, v, wq, wk, wv, a, b, S0, 4, 1)
+    out2, st2 = o.hybrid_layer(q, k, v, *maps, a, b, S0, 4, 1)
+    assert np.allclose(out, out2, rtol=1e-12, atol=1e-12) and np.allclose(st, st2, rtol=1e-12, atol=1e-12)
+
+
+def check_fmap_permutation(o):
+    """A permutation matrix as every map: Q' is Q with its channels reordered
+    (a cyclic shift, which a transposed map would shift the other way)."""
+    rng = np.random.default_rng(22)
+    q, k, v, _, a, b, S0 = _fmap_inputs(rng, H=2, d=4)
+    d = q.shape[3]
+    P = np.zeros((d, d))
+    for j in range(d):
+        P[j, (j + 1) % d] = 1.0  # e = j + 1: Q'[..., e] = Q[..., e - 1]
+    W = np.stack([P, P])
+    qp, kp, vp = o.feature_maps(q, k, v, W, W, W)
+    assert np.array_equal(qp, np.roll(q, 1, axis=3))
+    assert np.array_equal(kp, np.roll(k, 1, axis=3)) and np.array_equal(vp, np.roll(v, 1, axis=3))
+
+
+def check_fmap_grouped_by_head(o):
+    """Each head uses its own maps: changing head 1's maps leaves head 0's
+    outputs and state unchanged and changes head 1's."""
+    rng = np.random.default_rng(23)
+    q, k, v, (wq, wk, wv), a, b, S0 = _fmap_inputs(rng, H=2)
+    out, st = o.hybrid_layer_fmap(q, k, v, wq, wk, wv, a, b, S0, 4, 1)
+    for i in range(3):
+        w2 = [wq.copy(), wk.copy(), wv.copy()]
+        w2[i][1] = rng.standard_normal(w2[i][1].shape)
+        out2, st2 = o.hybrid_layer_fmap(q, k, v, *w2, a, b, S0, 4, 1)
+        assert np.array_equal(out2[:, :, 0], out[:, :, 0]) and np.array_equal(st2[:, 0], st[:, 0])
+        assert not np.allclose(out2[:, :, 1], out[:, :, 1])
+
+
+def check_fmap_fold(o):
+    """The identities the GPU path folds the maps with (exact algebra):
+    Q'S = Q (W_q S), and one clean frame gives
+    S_N = (alpha I - W_k^T G0 W_k) S + W_k^T B0 W_v with G0 = K^T diag(beta) K,
+    B0 = K^T diag(beta) V of the unmapped K, V."""
+    rng = np.random.default_rng(24)
+    q, k, v, (wq, wk, wv), a, b, S0 = _fmap_inputs(rng, B=1, T=4, H=1, d=4, L=4)
+    S = S0[0, 0] + 0.3 * rng.standard_normal(S0[0, 0].shape)
+    S0 = S[None, None]
+    out, st = o.hybrid_layer_fmap(q, k, v, wq, wk, wv, a, b, S0, 4, 1)
+    K, V, Q = k[0, :, 0], v[0, :, 0], q[0, :, 0]
+    G0 = K.T @ (b[0, :, 0][:, None] * K)
+    B0 = K.T @ (b[0, :, 0][:, None] * V)
+    Wq, Wk, Wv = wq[0], wk[0], wv[0]
+    want_S = (a[0, 0, 0] * np.eye(4) - Wk.T @ G0 @ Wk) @ S + Wk.T @ B0 @ Wv
+    assert np.allclose(st[0, 0], want_S, rtol=1e-10, atol=1e-12)
+    intra = o.intra_frame_attention(Q, K, V)
+    assert np.allclose(out[0, :, 0], intra + Q @ (Wq @ S), rtol=1e-10, atol=1e-12)
+
+
 ALL_CHECKS = [
+    check_fmap_brute_force,
+    check_fmap_permutation,
+    check_fmap_grouped_by_head,
+    check_fmap_fold,
     check_softmax_rows_sum_to_one,
     check_hand_worked_example,
     check_single_frame_is_textbook_attention,

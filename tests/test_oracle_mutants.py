@@ -103,7 +103,41 @@ def _layer_head_variant(m, read_after_update=False, global_attention=False,
     m.hybrid_layer_head = f
 
 
+def m_fmap_transposed(m):
+    def f(q, k, v, wq, wk, wv):
+        out = []
+        for x, w in ((q, wq), (k, wk), (v, wv)):
+            y = np.empty_like(x)
+            for h in range(x.shape[2]):
+                y[:, :, h, :] = x[:, :, h, :] @ w[h].T
+            out.append(y)
+        return tuple(out)
+    m.feature_maps = f
+
+
+def m_fmap_head0(m):
+    def f(q, k, v, wq, wk, wv):
+        return tuple(np.einsum("bthd,de->bthe", x, w[0]) for x, w in ((q, wq), (k, wk), (v, wv)))
+    m.feature_maps = f
+
+
+def m_fmap_wk_for_v(m):
+    orig = m.feature_maps
+    m.feature_maps = lambda q, k, v, wq, wk, wv: orig(q, k, v, wq, wk, wk)
+
+
+def m_fmap_maps_intra_branch(m):
+    def f(q, k, v, wq, wk, wv, alpha, beta, state, frame_len, update_state, scale=None):
+        qp, kp, vp = m.feature_maps(q, k, v, wq, wk, wv)
+        return m.hybrid_layer(qp, kp, vp, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale)
+    m.hybrid_layer_fmap = f
+
+
 MUTANTS = {
+    "fmap_transposed": m_fmap_transposed,
+    "fmap_head0_for_all": m_fmap_head0,
+    "fmap_wk_for_v": m_fmap_wk_for_v,
+    "fmap_maps_intra_branch": m_fmap_maps_intra_branch,
     "no_transpose": m_no_transpose,
     "decayed_residual": m_decayed_residual,
     "update_sign": m_sign,
