@@ -134,6 +134,43 @@ ha_status hybrid_attn_state_update(const void* kp, const void* vp,
                                    int B, int H, int T, int d, int frame_len,
                                    ha_dtype dtype, void* stream);
 
+/*
+ * Bytes of workspace hybrid_attn_forward_fmap needs (always at least the
+ * readout fragments): with update_state = 0, d x d bf16 per (stream, head);
+ * otherwise per (stream, head, frame) the state increments (d x 2d fp32), the
+ * fp32 partial sums of n token splits (n as for hybrid_attn_workspace_bytes,
+ * at least 1; d x 2d fp32 each), the pre-update state S_{N-1} (d x d fp32) and
+ * its readout fragments (d x d bf16), each region 256-byte aligned. Returns 0
+ * for invalid sizes.
+ */
+size_t hybrid_attn_fmap_workspace_bytes(int B, int H, int T, int frame_len, int d,
+                                        int update_state);
+
+/*
+ * The layer with the inter-frame branch's feature maps applied inside the
+ * call (ARL2 2.1, "adaptation": grouped per-head 1x1 maps phi_q, phi_k, phi_v
+ * of the frozen projections' Q, K, V), taken as one d x d linear map per head:
+ *   Q' = Q W_q, K' = K W_k, V' = V W_v  (row vectors; no bias, no nonlinearity)
+ * and otherwise exactly hybrid_attn_forward with those Q', K', V'. Q', K', V'
+ * are never formed: the readout uses Q (W_q S_{N-1}) and the state update the
+ * increments W_k^T G0 W_k and W_k^T B0 W_v of the unmapped K, V.
+ *   wq, wk, wv   [H, d, d] bf16, map of head h at w + h*d*d, row-major
+ *                (entry [j][e] multiplies input channel j into output e)
+ *   workspace    at least hybrid_attn_fmap_workspace_bytes(...); required
+ *                also when update_state is 0
+ * bf16 only (HA_ERR_UNSUPPORTED for HA_FP32). When update_state is 0, wk, wv,
+ * alpha and beta may be NULL. Other arguments, errors and stream behaviour
+ * as for hybrid_attn_forward.
+ */
+ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v,
+                                   const void* wq, const void* wk, const void* wv,
+                                   const float* alpha, const float* beta,
+                                   float* state, void* out,
+                                   void* workspace, size_t workspace_bytes,
+                                   int B, int H, int T, int d, int frame_len,
+                                   ha_dtype dtype, int update_state,
+                                   float softmax_scale, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* hybrid_attn_status_string(int status);
 

@@ -15,7 +15,8 @@ STATUS = {0: "HA_OK", 1: "HA_ERR_NULL", 2: "HA_ERR_SHAPE", 3: "HA_ERR_UNSUPPORTE
           4: "HA_ERR_ALIGN", 5: "HA_ERR_WORKSPACE", 6: "HA_ERR_DEVICE", 7: "HA_ERR_ALIAS"}
 EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_intra_readout",
            "hybrid_attn_state_update", "hybrid_attn_state_workspace_bytes",
-           "hybrid_attn_status_string", "hybrid_attn_version")
+           "hybrid_attn_status_string", "hybrid_attn_version", "hybrid_attn_forward_fmap",
+           "hybrid_attn_fmap_workspace_bytes")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_attn.so")
 _lib = None
@@ -47,6 +48,10 @@ def lib() -> ctypes.CDLL:
     L.hybrid_attn_state_update.restype = i
     L.hybrid_attn_state_workspace_bytes.argtypes = [i, i, i, i, i]
     L.hybrid_attn_state_workspace_bytes.restype = sz
+    L.hybrid_attn_forward_fmap.argtypes = [vp] * 10 + [vp, sz, i, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_forward_fmap.restype = i
+    L.hybrid_attn_fmap_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.hybrid_attn_fmap_workspace_bytes.restype = sz
     L.hybrid_attn_status_string.argtypes = [i]
     L.hybrid_attn_status_string.restype = ctypes.c_char_p
     L.hybrid_attn_version.argtypes = []
@@ -139,6 +144,51 @@ def hybrid_attn_forward(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, upda
         float(softmax_scale), _stream(dev))
     if st != 0:
         raise HybridAttnError(st, "hybrid_attn_forward")
+    return out
+
+
+def fmap_workspace_bytes(B, H, T, frame_len, d, update_state) -> int:
+    return int(lib().hybrid_attn_fmap_workspace_bytes(B, H, T, frame_len, d, int(bool(update_state))))
+
+
+def hybrid_attn_forward_fmap(q, k, v, wq, wk, wv, alpha, beta, state, frame_len, update_state,
+                             softmax_scale: float = 0.0, out=None, workspace=None):
+    """The layer with the per-head feature maps W_q, W_k, W_v ([H, d, d], same
+    dtype as q) applied inside the call: as hybrid_attn_forward with
+    Q' = Q W_q, K' = K W_k, V' = V W_v, none of which is materialised."""
+    torch = _torch()
+    if q.device.type != "cuda":
+        raise ValueError("hybrid_attn_forward_fmap runs on a GPU; tensors must be on a cuda device")
+    B, T, H, d = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    F = T // frame_len if frame_len > 0 and T % frame_len == 0 else -1
+    if F <= 0:
+        raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    _check("wq", wq, (H, d, d), dt, dev)
+    _check("state", state, (B, H, d, d), torch.float32, dev)
+    if update_state:
+        for name, t in (("wk", wk), ("wv", wv)):
+            _check(name, t, (H, d, d), dt, dev)
+        _check("alpha", alpha, (B, F, H), torch.float32, dev)
+        _check("beta", beta, (B, T, H), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, T, H, d), dt, dev)
+    need = fmap_workspace_bytes(B, H, T, frame_len, d, update_state)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().hybrid_attn_forward_fmap(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk if update_state else None),
+        _ptr(wv if update_state else None), _ptr(alpha if update_state else None),
+        _ptr(beta if update_state else None), _ptr(state), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, d, frame_len, code,
+        int(bool(update_state)), float(softmax_scale), _stream(dev))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_forward_fmap")
     return out
 
 

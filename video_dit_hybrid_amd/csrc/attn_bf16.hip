@@ -378,7 +378,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   if (sfrag) {
     constexpr int NSEG = D * D * 2 / 1024;  // 1 KB fragments
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(sfrag + ((size_t)(b * H + h) * F + n) * (size_t)D * D * 2, D * D * 2);
+        make_rsrc(sfrag + (size_t)(b * H + h) * stride_bh + (size_t)n * stride_frame, D * D * 2);
 #pragma unroll
     for (int i = wave; i < NSEG; i += NW) dma16_to_lds(rs, smem + i * 1024, lane * 16, i * 1024);
     __builtin_amdgcn_s_waitcnt(0);

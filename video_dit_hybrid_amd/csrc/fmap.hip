@@ -1,0 +1,288 @@
+// The grouped per-head 1x1 feature maps of the inter-frame branch (ARL2,
+// "Attend Locally, Remember Linearly", section 2.1 "adaptation": phi_q, phi_k,
+// phi_v adapt the frozen projections' Q, K, V to the linear recurrence), read
+// as one d x d linear map per head: Q' = Q W_q, K' = K W_k, V' = V W_v.
+//
+// The maps are folded into the work the layer already does instead of
+// materialising Q', K', V':
+//   readout   Q' S_{N-1} = Q (W_q S_{N-1})          -> mfrag_kernel writes the
+//             readout fragments of M = W_q S; the attention kernel reads Q.
+//   update    K'^T diag(beta) K' = W_k^T G0 W_k,
+//             K'^T diag(beta) V' = W_k^T B0 W_v,
+//             G0, B0 the increments of the unmapped K, V  -> gram_fmap_kernel
+//             turns the gram pass's fp32 G0, B0 into the scan's format.
+//
+// Operands: every fp32 matrix entering an MFMA is split into bf16 hi + lo (two
+// MFMAs), the maps are bf16 (exact); accumulation in fp32. All MFMA operands
+// use the contraction order of the scan's fragments: k-slot 8*hh + e of k-step
+// ks holds k = 16*ks + 8*(e/4) + 4*hh + e%4 (hh = lane / 32), in which the
+// accumulator registers [8s, 8s+8) of a 32x32 block are the operand of k-step
+// 2*(row band) + s.
+#include "ha_device.h"
+#include "ha_gram_format.h"
+#include "ha_launch.h"
+
+namespace ha {
+namespace {
+
+// eight fp32 -> bf16 hi + lo (hi = bf16(x), lo = bf16(x - hi))
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const uint32_t hp = pack_bf16x2(x[2 * w2], x[2 * w2 + 1]);
+    hi[w2] = hp;
+    lo[w2] = pack_bf16x2(x[2 * w2] - bf16_lo_to_f32(hp), x[2 * w2 + 1] - bf16_hi_to_f32(hp));
+  }
+}
+
+// W (bf16 [D][D] row-major) staged in LDS with the transposed-read swizzle;
+// wtr returns the MFMA operand of k-step ks and 32-column block cb:
+// lane l gets W[k][32*cb + l%32] for the eight k of its slots (two transposed
+// 4 x 16 reads, rows 16*ks + 4*hh + i/4 and those + 8).
+template <int D>
+__device__ __forceinline__ void stage_w(unsigned char* lds, const uint16_t* w, int tid, int nthreads) {
+  constexpr int NCH = D / 8;
+  for (int i = tid; i < D * NCH; i += nthreads) {
+    const int row = i / NCH, c = i % NCH;
+    const u32x4 x = ld_global_16B(w + (size_t)row * D + c * 8);
+    *reinterpret_cast<u32x4*>(lds + row * D * 2 + ((c ^ tr_swz<NCH>(row)) << 4)) = x;
+  }
+}
+template <int D>
+__device__ __forceinline__ u32x4 wtr(const unsigned char* lds, int ks, int cb, int lane) {
+  constexpr int NCH = D / 8;
+  const int gi = lane & 15, g = lane >> 4, hh = lane >> 5;
+  const int col = 32 * cb + 16 * (g & 1) + 4 * (gi & 3);
+  auto off = [&](int row) { return row * D * 2 + (((col >> 3) ^ tr_swz<NCH>(row)) << 4) + (col & 7) * 2; };
+  const int r0 = 16 * ks + 4 * hh + (gi >> 2);
+  const u32x2 x0 = ds_read_tr16(lds + off(r0));
+  const u32x2 x1 = ds_read_tr16(lds + off(r0 + 8));
+  return u32x4{x0[0], x0[1], x1[0], x1[1]};
+}
+
+// fp32 [D][D] row-major in LDS, 16-byte chunks XOR-swizzled by the row, so
+// that 32 lanes reading 16 bytes of 32 different rows hit distinct banks
+template <int D>
+__device__ __forceinline__ int xrow(int row, int col) {
+  constexpr int NC4 = D / 4;
+  return row * D + ((((col >> 2) ^ (row & (NC4 - 1)))) << 2) + (col & 3);
+}
+
+// One work-group (D/32 waves) per (b, h, frame), in the gram grid's order
+// hf = (b*F + n)*H + h. Wave w computes row band w of every product.
+//   T_G = G0 W_k : A = G0's column block w (G0 is symmetric), B = W_k
+//   G   = W_k^T T_G : A = W_k^T band w (= W_k column block w), B = T_G via LDS
+//   T_B = B0 W_v : A = B0 band w (rows from LDS), B = W_v
+//   B   = W_k^T T_B
+template <int D>
+__global__ __launch_bounds__(D / 32 * 64) void gram_fmap_kernel(const float* __restrict__ partial,
+                                                                int nsplit,
+                                                                const uint16_t* __restrict__ wk,
+                                                                const uint16_t* __restrict__ wv,
+                                                                float* __restrict__ gram, int H, int F) {
+  constexpr int NRB = D / 32, KS = D / 16, NTH = NRB * 64;
+  __shared__ __align__(16) unsigned char smem[2 * D * D * 2 + D * D * 4];
+  unsigned char* const wkl = smem;
+  unsigned char* const wvl = smem + D * D * 2;
+  float* const X = reinterpret_cast<float*>(smem + 2 * D * D * 2);
+  f32x4* const Xf = reinterpret_cast<f32x4*>(X);  // fragment layout [band][cb][v4][lane]
+
+  const int hf = blockIdx.x;
+  const int h = hf % H, n = (hf / H) % F, b = hf / (H * F);
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  stage_w<D>(wkl, wk + (size_t)h * D * D, tid, NTH);
+  stage_w<D>(wvl, wv + (size_t)h * D * D, tid, NTH);
+
+  auto sum_partial = [&](int rb, int cb, int gb) {  // sum over splits, split order
+    f32x16 r = f32x16{};
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const f32x4* src = partial_block<D>(const_cast<float*>(partial), (size_t)hf * nsplit + sp, rb, cb);
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const f32x4 x = src[(gb * 4 + v4) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[4 * v4 + e] += x[e];
+      }
+    }
+    return r;
+  };
+  auto frags_to_lds = [&](const f32x16* t) {
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        Xf[((w * NRB + cb) * 4 + v4) * 64 + lane] =
+            f32x4{t[cb][4 * v4], t[cb][4 * v4 + 1], t[cb][4 * v4 + 2], t[cb][4 * v4 + 3]};
+  };
+  // acc[cb] += W_k^T (band w) * Y, Y (fp32) in fragment layout in LDS
+  auto left_wkt = [&](f32x16* acc) {
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) acc[cb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 a = wtr<D>(wkl, ks, w, lane);
+      const int rb = ks >> 1, s = ks & 1;
+#pragma unroll
+      for (int cb = 0; cb < NRB; ++cb) {
+        const f32x4 y0 = Xf[((rb * NRB + cb) * 4 + 2 * s) * 64 + lane];
+        const f32x4 y1 = Xf[((rb * NRB + cb) * 4 + 2 * s + 1) * 64 + lane];
+        const float y8[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+        u32x4 bhi, blo;
+        split8(y8, bhi, blo);
+        acc[cb] = mfma32x32x16(a, bhi, acc[cb]);
+        acc[cb] = mfma32x32x16(a, blo, acc[cb]);
+      }
+    }
+  };
+  unsigned char* const base = reinterpret_cast<unsigned char*>(gram) +
+                              ((size_t)(b * H + h) * F + n) * (size_t)D * D * 8;
+
+  // ---- G = W_k^T (G0 W_k)
+  f32x16 t[NRB];
+  {
+    f32x16 g0[NRB];  // G0 blocks (rb, column block w) = G0 band w, transposed
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) g0[rb] = sum_partial(rb, w, 0);
+    __syncthreads();  // the maps are staged
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) t[cb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float a8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a8[e] = g0[ks >> 1][8 * (ks & 1) + e];
+      u32x4 ahi, alo;
+      split8(a8, ahi, alo);
+#pragma unroll
+      for (int cb = 0; cb < NRB; ++cb) {
+        const u32x4 bk = wtr<D>(wkl, ks, cb, lane);
+        t[cb] = mfma32x32x16(ahi, bk, t[cb]);
+        t[cb] = mfma32x32x16(alo, bk, t[cb]);
+      }
+    }
+  }
+  frags_to_lds(t);
+  __syncthreads();
+  left_wkt(t);
+#pragma unroll
+  for (int cb = 0; cb < NRB; ++cb)
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      float g8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g8[e] = t[cb][8 * sh + e];
+      store_g_half<D>(base, w, cb, sh, lane, g8);
+    }
+  __syncthreads();  // X is reused
+
+  // ---- B = W_k^T (B0 W_v); B0 row-major in LDS (its band w is not a
+  // column block of anything in registers)
+#pragma unroll
+  for (int cb = 0; cb < NRB; ++cb) {
+    const f32x16 x = sum_partial(w, cb, 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      X[xrow<D>(32 * w + 8 * (r >> 2) + 4 * hh + (r & 3), 32 * cb + lr)] = x[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int cb = 0; cb < NRB; ++cb) t[cb] = f32x16{};
+  const int arow = 32 * w + lr;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c0 = 16 * ks + 4 * hh;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(X + xrow<D>(arow, c0));
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(X + xrow<D>(arow, c0 + 8));
+    const float a8[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    u32x4 ahi, alo;
+    split8(a8, ahi, alo);
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) {
+      const u32x4 bv = wtr<D>(wvl, ks, cb, lane);
+      t[cb] = mfma32x32x16(ahi, bv, t[cb]);
+      t[cb] = mfma32x32x16(alo, bv, t[cb]);
+    }
+  }
+  __syncthreads();  // every wave has read B0
+  frags_to_lds(t);
+  __syncthreads();
+  left_wkt(t);
+#pragma unroll
+  for (int cb = 0; cb < NRB; ++cb)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4)
+      store_b4<D>(base, w, cb, v4, lane, f32x4{t[cb][4 * v4], t[cb][4 * v4 + 1], t[cb][4 * v4 + 2], t[cb][4 * v4 + 3]});
+}
+
+// Readout fragments of M = W_q S for one (b, h, frame, 32-column block cb):
+// wave w computes row band w of M[:, cb]; the fragment layout is the scan's
+// ([b*H + h][frame][cb][k-step][lane] x 16 bytes, bf16 of the band's
+// accumulator registers [8s, 8s+8) as k-step 2*w + s). S is fp32 row-major at
+// states + (b*H + h)*sbh + n*sfr (floats).
+template <int D>
+__global__ __launch_bounds__(D / 32 * 64) void mfrag_kernel(const float* __restrict__ states, long long sbh,
+                                                            long long sfr, const uint16_t* __restrict__ wq,
+                                                            u32x4* __restrict__ mfrag, int H, int Fe) {
+  constexpr int NCB = D / 32, KS = D / 16;
+  const int blk = blockIdx.x;
+  const int cb = blk % NCB, bhn = blk / NCB;
+  const int n = bhn % Fe, bh = bhn / Fe, h = bh % H;
+  const int lane = threadIdx.x & 63, lr = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const float* S = states + (size_t)bh * sbh + (size_t)n * sfr;
+  const uint16_t* W = wq + (size_t)h * D * D + (size_t)(32 * w + lr) * D;
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c0 = 16 * ks + 4 * hh;
+    const u32x2 a0 = *reinterpret_cast<const u32x2*>(W + c0);
+    const u32x2 a1 = *reinterpret_cast<const u32x2*>(W + c0 + 8);
+    const u32x4 a = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    float b8[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      b8[e] = S[(size_t)(c0 + e) * D + 32 * cb + lr];
+      b8[4 + e] = S[(size_t)(c0 + 8 + e) * D + 32 * cb + lr];
+    }
+    u32x4 bhi, blo;
+    split8(b8, bhi, blo);
+    acc = mfma32x32x16(a, bhi, acc);
+    acc = mfma32x32x16(a, blo, acc);
+  }
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh) {
+    u32x4 hi;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) hi[w2] = pack_bf16x2(acc[8 * sh + 2 * w2], acc[8 * sh + 2 * w2 + 1]);
+    mfrag[(((size_t)bhn * NCB + cb) * KS + 2 * w + sh) * 64 + lane] = hi;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gram_fmap(const float* partial, int nsplit, const void* wk, const void* wv, float* gram,
+                            const Shape& s, hipStream_t st) {
+  const int groups = s.B * s.H * s.F;
+  if (s.d == 128)
+    gram_fmap_kernel<128><<<groups, 256, 0, st>>>(partial, nsplit, (const uint16_t*)wk, (const uint16_t*)wv,
+                                                  gram, s.H, s.F);
+  else
+    gram_fmap_kernel<64><<<groups, 128, 0, st>>>(partial, nsplit, (const uint16_t*)wk, (const uint16_t*)wv,
+                                                 gram, s.H, s.F);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfrag(const float* states, long long sbh, long long sfr, const void* wq, void* mfrag, int frames,
+                        const Shape& s, hipStream_t st) {
+  const int ncb = s.d / 32;
+  const int groups = s.B * s.H * frames * ncb;
+  if (s.d == 128)
+    mfrag_kernel<128><<<groups, 256, 0, st>>>(states, sbh, sfr, (const uint16_t*)wq, (u32x4*)mfrag, s.H, frames);
+  else
+    mfrag_kernel<64><<<groups, 128, 0, st>>>(states, sbh, sfr, (const uint16_t*)wq, (u32x4*)mfrag, s.H, frames);
+  return hipGetLastError();
+}
+
+}  // namespace ha

@@ -13,8 +13,9 @@ struct Shape {
 
 // Intra-frame softmax + Q'S readout, bf16 operands on MFMA. The state of
 // (b, h, frame n) is either fp32 row-major at states + b*H*stride_bh... (see
-// hybrid_attn.h), or, when sfrag is not null, bf16 readout fragments at
-// sfrag + ((b*H + h)*F + n) * d*d (the layout state_scan writes, below).
+// hybrid_attn.h), or, when sfrag is not null, d x d bf16 readout fragments
+// (the layout state_scan writes, below) at sfrag + (b*H + h)*stride_bh +
+// n*stride_frame, the two strides then counted in bytes.
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const void* qp,
                             const float* states, long long stride_bh, long long stride_frame,
                             const void* sfrag, void* out, const Shape& s, float scale,
@@ -30,6 +31,18 @@ hipError_t launch_attn_fp32(const void* q, const void* k, const void* v, const v
 hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, float* gram,
                             const Shape& s, hipStream_t st);
 // fp32 path workspace, per (b, h, frame): [G | B] fp32 d x 2d.
+// The same pass writing only fp32 partial sums (partial_block layout of
+// ha_gram_format.h), nsplit token splits per (b, h, frame).
+hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float* beta,
+                                     float* partial, int nsplit, const Shape& s, hipStream_t st);
+// Feature maps (fmap.hip): the increments under K' = K W_k, V' = V W_v from the
+// partial sums of the unmapped K, V, written in the scan's format to gram;
+// and the readout fragments of M = W_q S for `frames` states per (b, h)
+// (fp32 row-major at states + (b*H + h)*sbh + n*sfr, in floats).
+hipError_t launch_gram_fmap(const float* partial, int nsplit, const void* wk, const void* wv, float* gram,
+                            const Shape& s, hipStream_t st);
+hipError_t launch_mfrag(const float* states, long long sbh, long long sfr, const void* wq, void* mfrag,
+                        int frames, const Shape& s, hipStream_t st);
 hipError_t launch_gram_fp32(const void* kp, const void* vp, const float* beta, float* gram,
                             const Shape& s, hipStream_t st);
 

@@ -201,12 +201,98 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
     // state to bf16 either way)
     r = run_update(kp, vp, alpha, beta, state, nullptr, gram, s, dtype, st, snap_area);
     if (r != HA_OK) return r;
-    return run_readout(q, k, v, qp, nullptr, 0, 0, out, s, dtype, scale, st, snap_area);
+    const long long fb = (long long)s.d * s.d * 2;  // fragment bytes per frame
+    return run_readout(q, k, v, qp, nullptr, (long long)s.F * fb, fb, out, s, dtype, scale, st, snap_area);
   }
   float* snaps = (float*)snap_area;
   r = run_update(kp, vp, alpha, beta, state, snaps, gram, s, dtype, st);
   if (r != HA_OK) return r;
   return run_readout(q, k, v, qp, snaps, (long long)s.F * dd, dd, out, s, dtype, scale, st);
+}
+
+// ---- feature-map variant (fmap.hip): the layer with Q' = Q W_q, K' = K W_k,
+// V' = V W_v folded into the kernels instead of materialised.
+//   update_state = 0 : M = W_q S once per (b, h), then the readout kernel on
+//                      Q and the fragments of M for every frame.
+//   update_state = 1 : gram pass on K, V (fp32 partial sums), the transform to
+//                      the increments under the maps, the scan (fp32
+//                      snapshots S_{n-1}, S_F into `state`), M_n = W_q S_{n-1}
+//                      for every frame, then the readout on Q and M_n.
+namespace {
+struct FmapWs {
+  size_t gram, partial, snaps, mfrag, total;
+};
+FmapWs fmap_layout(const ha::Shape& s, int update_state) {
+  FmapWs w{0, 0, 0, 0, 0};
+  const size_t dd = (size_t)s.d * s.d;
+  if (!update_state) {
+    w.mfrag = 0;
+    w.total = align_up((size_t)s.B * s.H * dd * 2);
+    return w;
+  }
+  const size_t gf = ha::gram_final_bytes(s);
+  w.gram = 0;
+  w.partial = align_up(gf);
+  w.snaps = w.partial + align_up(gf * ha::gram_splits(s));
+  w.mfrag = w.snaps + align_up((size_t)s.B * s.H * s.F * dd * 4);
+  w.total = w.mfrag + align_up((size_t)s.B * s.H * s.F * dd * 2);
+  return w;
+}
+}  // namespace
+
+size_t hybrid_attn_fmap_workspace_bytes(int B, int H, int T, int frame_len, int d, int update_state) {
+  ha::Shape s;
+  if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK) return 0;
+  return fmap_layout(s, update_state).total;
+}
+
+ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v, const void* wq,
+                                   const void* wk, const void* wv, const float* alpha,
+                                   const float* beta, float* state, void* out, void* workspace,
+                                   size_t workspace_bytes, int B, int H, int T, int d,
+                                   int frame_len, ha_dtype dtype, int update_state,
+                                   float softmax_scale, void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (dtype != HA_BF16) return HA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !wq || !state || !out || !workspace) return HA_ERR_NULL;
+  if (update_state && (!wk || !wv || !alpha || !beta)) return HA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(wq, 16) ||
+      !aligned(state, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+    return HA_ERR_ALIGN;
+  if (update_state && (!aligned(wk, 16) || !aligned(wv, 16) || !aligned(alpha, 4) || !aligned(beta, 4)))
+    return HA_ERR_ALIGN;
+  const FmapWs lay = fmap_layout(s, update_state);
+  if (workspace_bytes < lay.total) return HA_ERR_WORKSPACE;
+
+  const size_t tb = tensor_bytes(s, dtype);
+  const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
+  const size_t wb = (size_t)H * d * d * 2;
+  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
+      overlap(out, tb, wq, wb) || overlap(out, tb, state, stb) || overlap(out, tb, workspace, lay.total) ||
+      (update_state && (overlap(out, tb, wk, wb) || overlap(out, tb, wv, wb))))
+    return HA_ERR_ALIAS;
+
+  const float scale = resolve_scale(softmax_scale, d);
+  hipStream_t st = (hipStream_t)stream;
+  const long long dd = (long long)d * d, fb = dd * 2;
+  char* ws = (char*)workspace;
+  if (!update_state) {
+    void* mf = ws + lay.mfrag;
+    if (ha::launch_mfrag(state, dd, 0, wq, mf, 1, s, st) != hipSuccess) return HA_ERR_DEVICE;
+    return run_readout(q, k, v, q, nullptr, fb, 0, out, s, dtype, scale, st, mf);
+  }
+  float* gram = (float*)(ws + lay.gram);
+  float* partial = (float*)(ws + lay.partial);
+  float* snaps = (float*)(ws + lay.snaps);
+  void* mf = ws + lay.mfrag;
+  const int nsplit = ha::gram_splits(s);
+  if (ha::launch_gram_partials_bf16(k, v, beta, partial, nsplit, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  if (ha::launch_gram_fmap(partial, nsplit, wk, wv, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  if (ha::launch_state_scan_bf16(gram, alpha, state, snaps, nullptr, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  if (ha::launch_mfrag(snaps, (long long)s.F * dd, dd, wq, mf, s.F, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  return run_readout(q, k, v, q, nullptr, (long long)s.F * fb, fb, out, s, dtype, scale, st, mf);
 }
 
 }  // extern "C"

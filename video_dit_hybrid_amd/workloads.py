@@ -28,7 +28,7 @@ import numpy as np
 
 # tensor ids used in the seed sequence
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "qp": 3, "kp": 4, "vp": 5,
-              "alpha": 6, "beta": 7, "state": 8}
+              "alpha": 6, "beta": 7, "state": 8, "wq": 9, "wk": 10, "wv": 11}
 QKV_NAMES = ("q", "k", "v", "qp", "kp", "vp")
 
 
@@ -138,6 +138,20 @@ def make_state0(w: Workload) -> np.ndarray:
             g = _rng(w.cfg_id, "state", b, 0, 0)
             s[b] = g.normal(0.0, w.state0_sigma, size=(w.H, w.d, w.d)).astype(np.float32)
     return s
+
+
+def make_fmap_weights(w: Workload) -> dict:
+    """Per-head feature maps wq, wk, wv [H, d, d] for the feature-map variant,
+    N(0, 1) entries scaled so that the mapped tensors keep the statistics of
+    the plain workload's inputs when the unmapped ones are N(0, 1): wq and wv
+    by 1/sqrt(d) (Q', V' entries about N(0, 1)), wk by 1/d (K' rows of about
+    unit norm). Encoded like the other tensors (bf16 bits or fp32)."""
+    out = {}
+    for name, sc in (("wq", 1.0 / np.sqrt(w.d)), ("wk", 1.0 / w.d), ("wv", 1.0 / np.sqrt(w.d))):
+        g = _rng(w.cfg_id, name, 0, 0, 0)
+        x = (g.standard_normal((w.H, w.d, w.d)) * sc).astype(np.float32)
+        out[name] = _encode(x, w.dtype)
+    return out
 
 
 def _threads() -> int:
