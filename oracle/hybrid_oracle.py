@@ -31,7 +31,14 @@ Readings where the page is silent or garbled (each is listed in the design doc):
   * with update_state = 0 every frame reads the input state.
   * the feature maps phi_q, phi_k, phi_v (2.1, "adaptation": grouped per-head
     1x1 maps) are one d x d linear map per head, no bias, no nonlinearity,
-    applied to the inter-frame branch's inputs only.
+    applied to the inter-frame branch's inputs only;
+  * K' may be L2-normalised per (token, head) after its map (a flag; the page
+    names no normalisation; a zero row stays zero);
+  * the gates (2.1: alpha the forget gate, beta the step size, learned
+    per-token projections; ablations: headwise gating) are one projection per
+    head of the token's input x [C channels] plus a bias, through a sigmoid;
+    the frame's alpha_N is the mean of its tokens' alpha gates (one write per
+    frame), and beta_t is the token's gate divided by the frame length L.
 
 Every function here is pinned by tests/test_oracle_pins.py against
 properties the page and the mathematics fix (row sums, closed forms, the
@@ -147,7 +154,7 @@ def state_chain(kp, vp, alpha, beta, state, frame_len):
     return chain
 
 
-def feature_maps(q, k, v, wq, wk, wv):
+def feature_maps(q, k, v, wq, wk, wv, normalize_k=False):
     """The grouped per-head 1x1 feature maps of the inter-frame branch
     (ARL2 2.1, "adaptation": phi_q, phi_k, phi_v adapt the frozen projections'
     Q, K, V to the linear recurrence). Read here as one d x d linear map per
@@ -155,6 +162,8 @@ def feature_maps(q, k, v, wq, wk, wv):
     convolution grouped by head):
         Q'[b, t, h, :] = Q[b, t, h, :] @ wq[h]   (likewise K' with wk, V' with wv)
     q, k, v: [B, T, H, d] fp64; wq, wk, wv: [H, d, d] fp64.
+    With normalize_k, each row K'[b, t, h, :] is then divided by its L2 norm
+    (l2_normalize_rows).
     Returns (qp, kp, vp), each [B, T, H, d].
     """
     maps = []
@@ -163,7 +172,46 @@ def feature_maps(q, k, v, wq, wk, wv):
         for h in range(x.shape[2]):
             y[:, :, h, :] = x[:, :, h, :] @ w[h]
         maps.append(y)
+    if normalize_k:
+        maps[1] = l2_normalize_rows(maps[1])
     return tuple(maps)
+
+
+def l2_normalize_rows(x, eps=1e-12):
+    """x / max(||x||_2, eps) over the last axis (one key vector per token and
+    head); a zero row stays zero."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def sigmoid(z):
+    """1 / (1 + exp(-z)), fp64."""
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+
+
+def gate_projections(x, w_gate, b_gate, frame_len):
+    """The forget gate alpha and step size beta from the layer input (ARL2
+    2.1: learned per-token projections; headwise gating).
+
+    x: [B, T, C] fp64 (the tokens' input to the layer); w_gate: [2, H, C]
+    (row 0: alpha projections, row 1: beta projections, one per head);
+    b_gate: [2, H]. Per token t and head h:
+        a_t = sigmoid(x_t . w_gate[0, h] + b_gate[0, h])
+        g_t = sigmoid(x_t . w_gate[1, h] + b_gate[1, h])
+    alpha[b, N, h] = mean of a_t over the L tokens of frame N (the state is
+    written once per frame); beta[b, t, h] = g_t / L.
+    Returns (alpha [B, F, H], beta [B, T, H]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, T, C = x.shape
+    L = int(frame_len)
+    F = T // L
+    a = sigmoid(x @ np.asarray(w_gate[0], dtype=np.float64).T + np.asarray(b_gate[0], dtype=np.float64))
+    g = sigmoid(x @ np.asarray(w_gate[1], dtype=np.float64).T + np.asarray(b_gate[1], dtype=np.float64))
+    alpha = a.reshape(B, F, L, -1).mean(axis=2)
+    beta = g / L
+    return alpha, beta
 
 
 def hybrid_layer_fmap(q, k, v, wq, wk, wv, alpha, beta, state, frame_len,
@@ -174,3 +222,14 @@ def hybrid_layer_fmap(q, k, v, wq, wk, wv, alpha, beta, state, frame_len,
     projections). Returns (out, state_out) as hybrid_layer."""
     qp, kp, vp = feature_maps(q, k, v, wq, wk, wv)
     return hybrid_layer(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale)
+
+
+def hybrid_layer_gated(x, q, k, v, wq, wk, wv, w_gate, b_gate, state, frame_len,
+                       update_state, normalize_k=True, scale=None):
+    """The layer from its inputs as a transformer block holds them: the gates
+    from x (gate_projections), the feature maps (feature_maps, K' optionally
+    L2-normalised), then hybrid_layer. Returns (out, state_out, alpha, beta)."""
+    alpha, beta = gate_projections(x, w_gate, b_gate, frame_len)
+    qp, kp, vp = feature_maps(q, k, v, wq, wk, wv, normalize_k)
+    out, st = hybrid_layer(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale)
+    return out, st, alpha, beta

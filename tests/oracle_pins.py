@@ -369,7 +369,170 @@ def check_fmap_fold(o):
     assert np.allclose(out[0, :, 0], intra + Q @ (Wq @ S), rtol=1e-10, atol=1e-12)
 
 
+
+# --- gates and K' normalisation ---------------------------------------------
+
+def _gate_inputs(rng, B=2, T=8, C=5, H=2):
+    x = rng.standard_normal((B, T, C))
+    wg = rng.standard_normal((2, H, C)) / math.sqrt(C)
+    bg = rng.standard_normal((2, H))
+    return x, wg, bg
+
+
+def _brute_gates(x, wg, bg, L):
+    """alpha and beta by scalar loops and math.exp."""
+    B, T, C = x.shape
+    H = wg.shape[1]
+    F = T // L
+    alpha = np.zeros((B, F, H))
+    beta = np.zeros((B, T, H))
+    for bb in range(B):
+        for h in range(H):
+            for n in range(F):
+                acc = 0.0
+                for t in range(n * L, (n + 1) * L):
+                    za = bg[0, h]
+                    zb = bg[1, h]
+                    for c in range(C):
+                        za += x[bb, t, c] * wg[0, h, c]
+                        zb += x[bb, t, c] * wg[1, h, c]
+                    acc += 1.0 / (1.0 + math.exp(-za))
+                    beta[bb, t, h] = (1.0 / (1.0 + math.exp(-zb))) / L
+                alpha[bb, n, h] = acc / L
+    return alpha, beta
+
+
+def _brute_normalize(x):
+    y = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape[:-1]):
+        row = [float(e) for e in x[idx]]
+        nrm = math.sqrt(sum(e * e for e in row))
+        y[idx] = [e / max(nrm, 1e-12) for e in row]
+    return y
+
+
+def check_gates_brute_force(o):
+    """alpha = frame mean of sigmoid(x.w_alpha + b), beta = sigmoid(x.w_beta + b) / L,
+    per head, against scalar loops."""
+    rng = np.random.default_rng(31)
+    x, wg, bg = _gate_inputs(rng)
+    a, b = o.gate_projections(x, wg, bg, 4)
+    wa, wb = _brute_gates(x, wg, bg, 4)
+    assert a.shape == (2, 2, 2) and b.shape == (2, 8, 2)
+    assert np.allclose(a, wa, rtol=1e-13, atol=1e-15) and np.allclose(b, wb, rtol=1e-13, atol=1e-15)
+
+
+def check_gates_zero_projection(o):
+    """Zero weights and biases: every gate is sigmoid(0) = 1/2 exactly, so
+    alpha = 1/2 and beta = 1/(2L)."""
+    rng = np.random.default_rng(32)
+    x, wg, bg = _gate_inputs(rng, T=12)
+    a, b = o.gate_projections(x, 0 * wg, 0 * bg, 4)
+    assert np.all(a == 0.5) and np.all(b == 0.125)
+
+
+def check_gates_constant_frame(o):
+    """A frame whose tokens are all equal has alpha equal to that token's
+    gate (the mean of equal values): sigmoid(x.w + b) by hand."""
+    rng = np.random.default_rng(33)
+    x, wg, bg = _gate_inputs(rng, B=1, T=8, C=3, H=2)
+    x[0, 4:8] = x[0, 5]
+    a, _ = o.gate_projections(x, wg, bg, 4)
+    for h in range(2):
+        z = bg[0, h] + sum(x[0, 5, c] * wg[0, h, c] for c in range(3))
+        assert abs(a[0, 1, h] - 1.0 / (1.0 + math.exp(-z))) < 1e-15
+
+
+def check_gates_token_permutation(o):
+    """Permuting the tokens inside a frame leaves alpha (a frame mean) and
+    permutes beta; gates of one head ignore the other heads' weights."""
+    rng = np.random.default_rng(34)
+    x, wg, bg = _gate_inputs(rng, B=1, T=8, C=6, H=3)
+    a, b = o.gate_projections(x, wg, bg, 4)
+    perm = np.array([2, 0, 3, 1, 4, 5, 6, 7])
+    a2, b2 = o.gate_projections(x[:, perm], wg, bg, 4)
+    assert np.allclose(a2, a, rtol=1e-14, atol=0) and np.array_equal(b2, b[:, perm])
+    wg2 = wg.copy()
+    wg2[:, 1] = rng.standard_normal(wg2[:, 1].shape)
+    a3, b3 = o.gate_projections(x, wg2, bg, 4)
+    for h in (0, 2):
+        assert np.array_equal(a3[..., h], a[..., h]) and np.array_equal(b3[..., h], b[..., h])
+    assert not np.allclose(a3[..., 1], a[..., 1]) and not np.allclose(b3[..., 1], b[..., 1])
+
+
+def check_key_normalisation(o):
+    """Normalised K' rows: scalar-loop division by the row's L2 norm; unit
+    norms; a zero row stays zero; scaling a token's K by c > 0 leaves K'."""
+    rng = np.random.default_rng(35)
+    q, k, v, (wq, wk, wv), _, _, _ = _fmap_inputs(rng, B=1, T=8, H=2, d=3)
+    k[0, 3, 1] = 0.0
+    _, kp, _ = o.feature_maps(q, k, v, wq, wk, wv, True)
+    _, raw, _ = o.feature_maps(q, k, v, wq, wk, wv)
+    assert np.allclose(kp, _brute_normalize(raw), rtol=1e-13, atol=1e-15)
+    nrm = np.sqrt((kp ** 2).sum(-1))
+    assert np.all(kp[0, 3, 1] == 0.0)
+    nrm[0, 3, 1] = 1.0
+    assert np.allclose(nrm, 1.0, rtol=0, atol=1e-14)
+    c = rng.uniform(0.1, 10.0, (1, 8, 2, 1))
+    qp2, kp2, vp2 = o.feature_maps(q, k * c, v, wq, wk, wv, True)
+    assert np.allclose(kp2, kp, rtol=1e-13, atol=1e-15)
+
+
+def check_gated_layer_wiring(o):
+    """hybrid_layer_gated = hybrid_layer on brute-force gates and brute-force
+    maps with K' (and only K') normalised; without the flag, K' is the plain map."""
+    rng = np.random.default_rng(36)
+    B, T, H, d, C, L = 1, 8, 2, 3, 5, 4
+    q, k, v, (wq, wk, wv), _, _, S0 = _fmap_inputs(rng, B=B, T=T, H=H, d=d, L=L)
+    x, wg, bg = _gate_inputs(rng, B=B, T=T, C=C, H=H)
+    wa, wb = _brute_gates(x, wg, bg, L)
+    maps = []
+    for xx, w in ((q, wq), (k, wk), (v, wv)):
+        y = np.zeros_like(xx)
+        for t in range(T):
+            for h in range(H):
+                for e in range(d):
+                    y[0, t, h, e] = sum(xx[0, t, h, j] * w[h][j, e] for j in range(d))
+        maps.append(y)
+    for norm in (True, False):
+        kk = _brute_normalize(maps[1]) if norm else maps[1]
+        out, st, a, b = o.hybrid_layer_gated(x, q, k, v, wq, wk, wv, wg, bg, S0, L, 1, norm)
+        out2, st2 = o.hybrid_layer(q, k, v, maps[0], kk, maps[2], wa, wb, S0, L, 1)
+        assert np.allclose(a, wa, rtol=1e-13, atol=1e-15) and np.allclose(b, wb, rtol=1e-13, atol=1e-15)
+        assert np.allclose(out, out2, rtol=1e-11, atol=1e-12) and np.allclose(st, st2, rtol=1e-11, atol=1e-12)
+
+
+def check_gated_fold_normalised(o):
+    """The identity the GPU path uses for normalised keys (exact algebra):
+    with n_t = ||K_t W_k||, one clean frame gives
+    S_N = (alpha I - W_k^T K^T diag(beta/n^2) K W_k) S + W_k^T K^T diag(beta/n) V W_v;
+    and the final state does not change when a token's K is scaled by c > 0."""
+    rng = np.random.default_rng(37)
+    L, d, C = 4, 4, 6
+    q, k, v, (wq, wk, wv), _, _, S0 = _fmap_inputs(rng, B=1, T=4, H=1, d=d, L=L)
+    x, wg, bg = _gate_inputs(rng, B=1, T=4, C=C, H=1)
+    S = S0[0, 0] + 0.3 * rng.standard_normal((d, d))
+    _, st, a, b = o.hybrid_layer_gated(x, q, k, v, wq, wk, wv, wg, bg, S[None, None], L, 1, True)
+    K, V, Wk, Wv = k[0, :, 0], v[0, :, 0], wk[0], wv[0]
+    n = np.sqrt(((K @ Wk) ** 2).sum(1))
+    bt = b[0, :, 0]
+    G0 = K.T @ ((bt / n ** 2)[:, None] * K)
+    B0 = K.T @ ((bt / n)[:, None] * V)
+    want = (a[0, 0, 0] * np.eye(d) - Wk.T @ G0 @ Wk) @ S + Wk.T @ B0 @ Wv
+    assert np.allclose(st[0, 0], want, rtol=1e-10, atol=1e-12)
+    c = rng.uniform(0.2, 5.0, (1, 4, 1, 1))
+    _, st2, _, _ = o.hybrid_layer_gated(x, q, k * c, v, wq, wk, wv, wg, bg, S[None, None], L, 1, True)
+    assert np.allclose(st2, st, rtol=1e-11, atol=1e-13)
+
+
 ALL_CHECKS = [
+    check_gates_brute_force,
+    check_gates_zero_projection,
+    check_gates_constant_frame,
+    check_gates_token_permutation,
+    check_key_normalisation,
+    check_gated_layer_wiring,
+    check_gated_fold_normalised,
     check_fmap_brute_force,
     check_fmap_permutation,
     check_fmap_grouped_by_head,

@@ -133,7 +133,75 @@ def m_fmap_maps_intra_branch(m):
     m.hybrid_layer_fmap = f
 
 
+
+def m_gates_swapped(m):
+    orig = m.gate_projections
+    m.gate_projections = lambda x, wg, bg, L: orig(x, wg[::-1], bg[::-1], L)
+
+
+def m_beta_not_over_frame_len(m):
+    orig = m.gate_projections
+    def f(x, wg, bg, L):
+        a, b = orig(x, wg, bg, L)
+        return a, b * L
+    m.gate_projections = f
+
+
+def m_alpha_first_token(m):
+    def f(x, wg, bg, L):
+        B, T, _ = x.shape
+        a = m.sigmoid(x @ wg[0].T + bg[0])
+        g = m.sigmoid(x @ wg[1].T + bg[1])
+        return a[:, ::L], g / L
+    m.gate_projections = f
+
+
+def m_alpha_sigmoid_of_mean_logit(m):
+    def f(x, wg, bg, L):
+        B, T, _ = x.shape
+        z = x @ wg[0].T + bg[0]
+        g = m.sigmoid(x @ wg[1].T + bg[1])
+        return m.sigmoid(z.reshape(B, T // L, L, -1).mean(axis=2)), g / L
+    m.gate_projections = f
+
+
+def m_gates_no_bias(m):
+    orig = m.gate_projections
+    m.gate_projections = lambda x, wg, bg, L: orig(x, wg, 0 * bg, L)
+
+
+def m_normalise_wrong_axis(m):
+    def f(x, eps=1e-12):
+        n = np.sqrt(np.sum(x * x, axis=1, keepdims=True))
+        return x / np.maximum(n, eps)
+    m.l2_normalize_rows = f
+
+
+def m_normalise_before_map(m):
+    orig = m.feature_maps
+    def f(q, k, v, wq, wk, wv, normalize_k=False):
+        kk = m.l2_normalize_rows(k) if normalize_k else k
+        return orig(q, kk, v, wq, wk, wv, False)
+    m.feature_maps = f
+
+
+def m_normalise_q_too(m):
+    orig = m.feature_maps
+    def f(q, k, v, wq, wk, wv, normalize_k=False):
+        qp, kp, vp = orig(q, k, v, wq, wk, wv, normalize_k)
+        return (m.l2_normalize_rows(qp) if normalize_k else qp), kp, vp
+    m.feature_maps = f
+
+
 MUTANTS = {
+    "gates_swapped": m_gates_swapped,
+    "beta_not_over_frame_len": m_beta_not_over_frame_len,
+    "alpha_first_token": m_alpha_first_token,
+    "alpha_sigmoid_of_mean_logit": m_alpha_sigmoid_of_mean_logit,
+    "gates_no_bias": m_gates_no_bias,
+    "normalise_wrong_axis": m_normalise_wrong_axis,
+    "normalise_before_map": m_normalise_before_map,
+    "normalise_q_too": m_normalise_q_too,
     "fmap_transposed": m_fmap_transposed,
     "fmap_head0_for_all": m_fmap_head0,
     "fmap_wk_for_v": m_fmap_wk_for_v,
