@@ -171,6 +171,67 @@ ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v,
                                    ha_dtype dtype, int update_state,
                                    float softmax_scale, void* stream);
 
+/*
+ * Bytes of workspace hybrid_attn_forward_gated needs: with update_state 0 the
+ * same as hybrid_attn_fmap_workspace_bytes; with update_state 1 that layout
+ * followed by beta, beta / n^2 and beta / n ([B, T, H] fp32 each), the
+ * per-chunk alpha sums of the gate pass and alpha ([B, F, H] fp32), each
+ * region 256-byte aligned. Returns 0 for invalid sizes.
+ */
+size_t hybrid_attn_gated_workspace_bytes(int B, int H, int T, int frame_len, int d,
+                                         int update_state);
+
+/*
+ * The layer from the inputs a transformer block holds: the gates come from
+ * the layer input x and the feature maps are applied inside the call.
+ * ARL2 2.1: alpha (forget gate) and beta (step size) are learned per-token
+ * projections, one per head (headwise gating, ablations of section 4); read
+ * here, per token t and head h, as
+ *   a_t = sigmoid(x_t . w_gate[0][h] + b_gate[0][h]),
+ *   g_t = sigmoid(x_t . w_gate[1][h] + b_gate[1][h]),
+ * alpha_N = the mean of a_t over the L tokens of frame N (the state is written
+ * once per frame), beta_t = g_t / L. Then, as hybrid_attn_forward_fmap,
+ * Q' = Q W_q, K' = K W_k, V' = V W_v, and with normalize_k != 0 each K' row
+ * divided by max(||K'_t||_2, 1e-12) (no normalisation is named on the page;
+ * unit keys are the delta rule's usual convention).
+ *   x        [B, T, C] bf16, C channels per token (C % 16 == 0)
+ *   w_gate   [2, H, C] bf16: row 0 the alpha projections, row 1 beta's
+ *   b_gate   [2, H] fp32
+ *   wq, wk, wv, q, k, v, state, out: as hybrid_attn_forward_fmap
+ *   workspace at least hybrid_attn_gated_workspace_bytes(...)
+ * bf16 only; H <= 64 when update_state is 1 (HA_ERR_UNSUPPORTED beyond).
+ * When update_state is 0 only the readout runs (M = W_q S); x, wk, wv,
+ * w_gate and b_gate may then be NULL and C is ignored. Errors and stream
+ * behaviour as for hybrid_attn_forward.
+ */
+ha_status hybrid_attn_forward_gated(const void* x, const void* q, const void* k, const void* v,
+                                    const void* wq, const void* wk, const void* wv,
+                                    const void* w_gate, const float* b_gate,
+                                    float* state, void* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    int B, int H, int T, int d, int C, int frame_len,
+                                    ha_dtype dtype, int update_state, int normalize_k,
+                                    float softmax_scale, void* stream);
+
+/*
+ * Bytes of workspace hybrid_attn_gates needs (the per-chunk alpha sums,
+ * B * F * ceil(L / 32) * H floats, 256-byte aligned). 0 for invalid sizes.
+ */
+size_t hybrid_attn_gates_workspace_bytes(int B, int H, int T, int frame_len);
+
+/*
+ * The gate projections of hybrid_attn_forward_gated alone: writes
+ * alpha [B, F, H] and beta [B, T, H] (fp32) from x [B, T, C] bf16,
+ * w_gate [2, H, C] bf16 and b_gate [2, H] fp32. alpha is the frame mean of
+ * the per-token gates, summed in a fixed order (equal inputs give bitwise
+ * equal results). bf16 only; C % 16 == 0; H <= 64. Outputs must not overlap
+ * the inputs or the workspace (HA_ERR_ALIAS). Asynchronous on `stream`.
+ */
+ha_status hybrid_attn_gates(const void* x, const void* w_gate, const float* b_gate,
+                            float* alpha, float* beta, void* workspace, size_t workspace_bytes,
+                            int B, int H, int T, int C, int frame_len, ha_dtype dtype,
+                            void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* hybrid_attn_status_string(int status);
 

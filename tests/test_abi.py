@@ -115,3 +115,66 @@ def test_python_binding_refuses_cpu_tensors():
     s = torch.zeros(1, 2, 64, 64)
     with pytest.raises(ValueError):
         api.hybrid_attn_forward(x, x, x, x, x, x, None, None, s, 32, 0)
+
+
+def test_feature_map_and_gated_workspace_sizes():
+    d, H, L, F = 128, 12, 1560, 21
+    T = F * L
+    up = lambda x: (x + 255) // 256 * 256
+    gf = H * F * d * 2 * d * 4
+    fmap1 = up(gf) + up(gf) + up(H * F * d * d * 4) + up(H * F * d * d * 2)
+    assert api.fmap_workspace_bytes(1, H, T, L, d, 0) == up(H * d * d * 2)
+    assert api.fmap_workspace_bytes(1, H, T, L, d, 1) == fmap1
+    # gated: beta, beta / n^2, beta / n, per-32-token-chunk alpha sums (49 chunks
+    # of a 1560-token frame), alpha
+    tok = up(T * H * 4)
+    assert api.gated_workspace_bytes(1, H, T, L, d, 1) == fmap1 + 3 * tok + up(F * 49 * H * 4) + up(F * H * 4)
+    assert api.gated_workspace_bytes(1, H, T, L, d, 0) == api.fmap_workspace_bytes(1, H, T, L, d, 0)
+    assert api.gates_workspace_bytes(1, H, T, L) == up(F * 49 * H * 4)
+    assert api.gated_workspace_bytes(1, H, T + 1, L, d, 1) == 0
+
+
+def gated(**kw):
+    a = dict(x=4096, q=8192, k=12288, v=16384, wq=20480, wk=24576, wv=28672, wg=32768, bg=36864,
+             state=40960, out=1 << 40, ws=1 << 41, ws_bytes=1 << 40, B=1, H=2, T=64, d=64, C=128, L=32,
+             dtype=0, update=1, norm=1, scale=0.0)
+    a.update(kw)
+    ptr = lambda x: None if x is None else P(x)
+    return api.lib().hybrid_attn_forward_gated(
+        ptr(a["x"]), ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["wq"]), ptr(a["wk"]), ptr(a["wv"]),
+        ptr(a["wg"]), ptr(a["bg"]), ptr(a["state"]), ptr(a["out"]), ptr(a["ws"]), a["ws_bytes"], a["B"],
+        a["H"], a["T"], a["d"], a["C"], a["L"], a["dtype"], a["update"], a["norm"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(wg=None), 1), (dict(bg=None), 1), (dict(wk=None), 1), (dict(q=None), 1),
+    (dict(C=0), 2), (dict(C=24), 2), (dict(T=65), 2),
+    (dict(H=65), 3), (dict(dtype=1), 3), (dict(d=96), 3),
+    (dict(x=4100), 4), (dict(wg=32772), 4), (dict(bg=36866), 4),
+    (dict(ws_bytes=100), 5),
+    (dict(out=4096), 7), (dict(out=32768), 7),
+])
+def test_gated_validation_codes(kw, code):
+    assert gated(**kw) == code
+
+
+def test_gated_denoise_pass_needs_no_gate_inputs():
+    # update_state = 0 reads neither x nor the gate weights nor wk, wv (and C
+    # is ignored); stop before device work with an invalid d
+    assert gated(x=None, wk=None, wv=None, wg=None, bg=None, C=0, update=0, d=96) == 3
+    assert gated(x=None, wk=None, wv=None, wg=None, bg=None, C=0, update=0, q=8196) == 4
+
+
+def test_gates_entry_validates():
+    L = api.lib()
+
+    def g(x=4096, wg=8192, bg=12288, al=16384, be=20480, ws=1 << 41, wsb=1 << 40, B=1, H=2, T=64, C=64,
+          Lf=32, dtype=0):
+        p = lambda v: None if v is None else P(v)
+        return L.hybrid_attn_gates(p(x), p(wg), p(bg), p(al), p(be), p(ws), wsb, B, H, T, C, Lf, dtype, None)
+    assert g(C=8) == 2 and g(T=65) == 2
+    assert g(al=None) == 1 and g(ws=None) == 1
+    assert g(H=65) == 3 and g(dtype=1) == 3
+    assert g(x=4097) == 4
+    assert g(wsb=4) == 5
+    assert g(be=16384 + 8) == 7

@@ -16,7 +16,8 @@ STATUS = {0: "HA_OK", 1: "HA_ERR_NULL", 2: "HA_ERR_SHAPE", 3: "HA_ERR_UNSUPPORTE
 EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_intra_readout",
            "hybrid_attn_state_update", "hybrid_attn_state_workspace_bytes",
            "hybrid_attn_status_string", "hybrid_attn_version", "hybrid_attn_forward_fmap",
-           "hybrid_attn_fmap_workspace_bytes")
+           "hybrid_attn_fmap_workspace_bytes", "hybrid_attn_forward_gated",
+           "hybrid_attn_gated_workspace_bytes", "hybrid_attn_gates", "hybrid_attn_gates_workspace_bytes")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_attn.so")
 _lib = None
@@ -52,6 +53,14 @@ def lib() -> ctypes.CDLL:
     L.hybrid_attn_forward_fmap.restype = i
     L.hybrid_attn_fmap_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.hybrid_attn_fmap_workspace_bytes.restype = sz
+    L.hybrid_attn_forward_gated.argtypes = [vp] * 11 + [vp, sz, i, i, i, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_forward_gated.restype = i
+    L.hybrid_attn_gated_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.hybrid_attn_gated_workspace_bytes.restype = sz
+    L.hybrid_attn_gates.argtypes = [vp] * 5 + [vp, sz, i, i, i, i, i, i, vp]
+    L.hybrid_attn_gates.restype = i
+    L.hybrid_attn_gates_workspace_bytes.argtypes = [i, i, i, i]
+    L.hybrid_attn_gates_workspace_bytes.restype = sz
     L.hybrid_attn_status_string.argtypes = [i]
     L.hybrid_attn_status_string.restype = ctypes.c_char_p
     L.hybrid_attn_version.argtypes = []
@@ -191,6 +200,91 @@ def hybrid_attn_forward_fmap(q, k, v, wq, wk, wv, alpha, beta, state, frame_len,
         raise HybridAttnError(st, "hybrid_attn_forward_fmap")
     return out
 
+
+
+def gated_workspace_bytes(B, H, T, frame_len, d, update_state) -> int:
+    return int(lib().hybrid_attn_gated_workspace_bytes(B, H, T, frame_len, d, int(bool(update_state))))
+
+
+def gates_workspace_bytes(B, H, T, frame_len) -> int:
+    return int(lib().hybrid_attn_gates_workspace_bytes(B, H, T, frame_len))
+
+
+def hybrid_attn_gates(x, w_gate, b_gate, H, frame_len, alpha=None, beta=None, workspace=None):
+    """alpha [B, F, H] and beta [B, T, H] (fp32) from the layer input x
+    [B, T, C] and the headwise gate projections w_gate [2, H, C] (x's dtype),
+    b_gate [2, H] fp32."""
+    torch = _torch()
+    if x.device.type != "cuda":
+        raise ValueError("hybrid_attn_gates runs on a GPU; tensors must be on a cuda device")
+    B, T, C = x.shape
+    dev = x.device
+    code = _dtype_code(x)
+    F = T // frame_len if frame_len > 0 and T % frame_len == 0 else -1
+    if F <= 0:
+        raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
+    _check("w_gate", w_gate, (2, H, C), x.dtype, dev)
+    _check("b_gate", b_gate, (2, H), torch.float32, dev)
+    if alpha is None:
+        alpha = torch.empty((B, F, H), dtype=torch.float32, device=dev)
+    if beta is None:
+        beta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    _check("alpha", alpha, (B, F, H), torch.float32, dev)
+    _check("beta", beta, (B, T, H), torch.float32, dev)
+    need = gates_workspace_bytes(B, H, T, frame_len)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().hybrid_attn_gates(_ptr(x), _ptr(w_gate), _ptr(b_gate), _ptr(alpha), _ptr(beta), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), B, H, T, C, frame_len, code,
+                                 _stream(dev))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_gates")
+    return alpha, beta
+
+
+def hybrid_attn_forward_gated(x, q, k, v, wq, wk, wv, w_gate, b_gate, state, frame_len, update_state,
+                              normalize_k=True, softmax_scale: float = 0.0, out=None, workspace=None):
+    """The layer with its gates projected from x [B, T, C] (w_gate [2, H, C],
+    b_gate [2, H] fp32) and the per-head feature maps applied inside the call
+    (K' L2-normalised per token when normalize_k); on a denoising pass
+    (update_state 0) x, wk, wv and the gate weights are not read."""
+    torch = _torch()
+    if q.device.type != "cuda":
+        raise ValueError("hybrid_attn_forward_gated runs on a GPU; tensors must be on a cuda device")
+    B, T, H, d = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    F = T // frame_len if frame_len > 0 and T % frame_len == 0 else -1
+    if F <= 0:
+        raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    _check("wq", wq, (H, d, d), dt, dev)
+    _check("state", state, (B, H, d, d), torch.float32, dev)
+    C = 0
+    if update_state:
+        C = x.shape[-1]
+        _check("x", x, (B, T, C), dt, dev)
+        for name, t in (("wk", wk), ("wv", wv)):
+            _check(name, t, (H, d, d), dt, dev)
+        _check("w_gate", w_gate, (2, H, C), dt, dev)
+        _check("b_gate", b_gate, (2, H), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, T, H, d), dt, dev)
+    need = gated_workspace_bytes(B, H, T, frame_len, d, update_state)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    u = bool(update_state)
+    st = lib().hybrid_attn_forward_gated(
+        _ptr(x if u else None), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk if u else None),
+        _ptr(wv if u else None), _ptr(w_gate if u else None), _ptr(b_gate if u else None), _ptr(state),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, d, C, frame_len,
+        code, int(u), int(bool(normalize_k)), float(softmax_scale), _stream(dev))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_forward_gated")
+    return out
 
 def hybrid_attn_intra_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame,
                               frame_len, softmax_scale: float = 0.0, out=None):

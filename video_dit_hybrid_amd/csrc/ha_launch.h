@@ -32,8 +32,9 @@ hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, f
                             const Shape& s, hipStream_t st);
 // fp32 path workspace, per (b, h, frame): [G | B] fp32 d x 2d.
 // The same pass writing only fp32 partial sums (partial_block layout of
-// ha_gram_format.h), nsplit token splits per (b, h, frame).
-hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float* beta,
+// ha_gram_format.h), nsplit token splits per (b, h, frame). With beta2 not
+// null the B increments use it: G = K'^T diag(beta) K', B = K'^T diag(beta2) V'.
+hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float* beta, const float* beta2,
                                      float* partial, int nsplit, const Shape& s, hipStream_t st);
 // Feature maps (fmap.hip): the increments under K' = K W_k, V' = V W_v from the
 // partial sums of the unmapped K, V, written in the scan's format to gram;
@@ -43,6 +44,17 @@ hipError_t launch_gram_fmap(const float* partial, int nsplit, const void* wk, co
                             const Shape& s, hipStream_t st);
 hipError_t launch_mfrag(const float* states, long long sbh, long long sfr, const void* wq, void* mfrag,
                         int frames, const Shape& s, hipStream_t st);
+// Step sizes for L2-normalised keys (fmap.hip): with n_t = ||K_t W_k||,
+// beta_g = beta / n^2 and beta_b = beta / n per (b, token, h), [B, T, H] fp32.
+hipError_t launch_keyscale(const void* k, const void* wk, const float* beta, float* beta_g, float* beta_b,
+                           const Shape& s, hipStream_t st);
+// Headwise gate projections (gates.hip) from x [B, T, C] bf16, w_gate [2, H, C]
+// bf16, b_gate [2, H] fp32: alpha [B, F, H], beta [B, T, H]; apart holds
+// gates_partial_bytes of per-chunk alpha sums.
+int gates_chunks(const Shape& s);
+size_t gates_partial_bytes(const Shape& s);
+hipError_t launch_gates(const void* x, const void* wg, const float* bg, float* alpha, float* beta, float* apart,
+                        int C, const Shape& s, hipStream_t st);
 hipError_t launch_gram_fp32(const void* kp, const void* vp, const float* beta, float* gram,
                             const Shape& s, hipStream_t st);
 

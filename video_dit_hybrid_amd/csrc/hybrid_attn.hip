@@ -1,6 +1,6 @@
 // C ABI of the hybrid attention layer: argument validation, workspace layout
 // and launch order. The kernels live in attn_bf16.hip, state_bf16.hip,
-// state_scan.hip and fp32_path.hip.
+// state_scan.hip, fp32_path.hip, fmap.hip and gates.hip.
 //
 // Launch order of a call (ARL2 section 2.2: every token of frame N reads
 // S_{N-1}; the state is written once per clean frame, after the frame):
@@ -210,6 +210,8 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
   return run_readout(q, k, v, qp, snaps, (long long)s.F * dd, dd, out, s, dtype, scale, st);
 }
 
+}  // extern "C"
+
 // ---- feature-map variant (fmap.hip): the layer with Q' = Q W_q, K' = K W_k,
 // V' = V W_v folded into the kernels instead of materialised.
 //   update_state = 0 : M = W_q S once per (b, h), then the readout kernel on
@@ -218,12 +220,17 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
 //                      the increments under the maps, the scan (fp32
 //                      snapshots S_{n-1}, S_F into `state`), M_n = W_q S_{n-1}
 //                      for every frame, then the readout on Q and M_n.
+// The gated variant (gates.hip) first computes alpha and beta from the layer
+// input x and, for normalised keys, the two step-size vectors beta / n^2 and
+// beta / n (keyscale), then runs the same passes.
 namespace {
 struct FmapWs {
-  size_t gram, partial, snaps, mfrag, total;
+  size_t gram, partial, snaps, mfrag;
+  size_t beta, beta_g, beta_b, apart, alpha;  // gated variant only
+  size_t total;
 };
-FmapWs fmap_layout(const ha::Shape& s, int update_state) {
-  FmapWs w{0, 0, 0, 0, 0};
+FmapWs fmap_layout(const ha::Shape& s, int update_state, bool gated) {
+  FmapWs w{};
   const size_t dd = (size_t)s.d * s.d;
   if (!update_state) {
     w.mfrag = 0;
@@ -236,14 +243,57 @@ FmapWs fmap_layout(const ha::Shape& s, int update_state) {
   w.snaps = w.partial + align_up(gf * ha::gram_splits(s));
   w.mfrag = w.snaps + align_up((size_t)s.B * s.H * s.F * dd * 4);
   w.total = w.mfrag + align_up((size_t)s.B * s.H * s.F * dd * 2);
+  if (gated) {
+    const size_t tok = (size_t)s.B * s.T * s.H * sizeof(float);
+    w.beta = w.total;
+    w.beta_g = w.beta + align_up(tok);
+    w.beta_b = w.beta_g + align_up(tok);
+    w.apart = w.beta_b + align_up(tok);
+    w.alpha = w.apart + align_up(ha::gates_partial_bytes(s));
+    w.total = w.alpha + align_up((size_t)s.B * s.F * s.H * sizeof(float));
+  }
   return w;
 }
+
+// The passes shared by the two variants; arguments already validated.
+ha_status fmap_run(const void* q, const void* k, const void* v, const void* wq, const void* wk, const void* wv,
+                   const float* alpha, const float* beta, const float* beta2, float* state, void* out,
+                   char* ws, const FmapWs& lay, const ha::Shape& s, int update_state, float scale,
+                   hipStream_t st) {
+  const long long dd = (long long)s.d * s.d, fb = dd * 2;
+  if (!update_state) {
+    void* mf = ws + lay.mfrag;
+    if (ha::launch_mfrag(state, dd, 0, wq, mf, 1, s, st) != hipSuccess) return HA_ERR_DEVICE;
+    return run_readout(q, k, v, q, nullptr, fb, 0, out, s, HA_BF16, scale, st, mf);
+  }
+  float* gram = (float*)(ws + lay.gram);
+  float* partial = (float*)(ws + lay.partial);
+  float* snaps = (float*)(ws + lay.snaps);
+  void* mf = ws + lay.mfrag;
+  const int nsplit = ha::gram_splits(s);
+  if (ha::launch_gram_partials_bf16(k, v, beta, beta2, partial, nsplit, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  if (ha::launch_gram_fmap(partial, nsplit, wk, wv, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  if (ha::launch_state_scan_bf16(gram, alpha, state, snaps, nullptr, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  if (ha::launch_mfrag(snaps, (long long)s.F * dd, dd, wq, mf, s.F, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  return run_readout(q, k, v, q, nullptr, (long long)s.F * fb, fb, out, s, HA_BF16, scale, st, mf);
+}
+
+// Shape checks of the gate projection: C channels in 16-element k-steps, at
+// most 64 heads (2H gate rows in four 32-row MFMA blocks).
+ha_status check_gate_shape(const ha::Shape& s, int C) {
+  if (C <= 0 || C % 16 != 0) return HA_ERR_SHAPE;
+  if (s.H > 64) return HA_ERR_UNSUPPORTED;
+  if ((long long)s.B * s.F * ha::gates_chunks(s) > kMaxItems) return HA_ERR_SHAPE;
+  return HA_OK;
+}
 }  // namespace
+
+extern "C" {
 
 size_t hybrid_attn_fmap_workspace_bytes(int B, int H, int T, int frame_len, int d, int update_state) {
   ha::Shape s;
   if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK) return 0;
-  return fmap_layout(s, update_state).total;
+  return fmap_layout(s, update_state, false).total;
 }
 
 ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v, const void* wq,
@@ -263,7 +313,7 @@ ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v, 
     return HA_ERR_ALIGN;
   if (update_state && (!aligned(wk, 16) || !aligned(wv, 16) || !aligned(alpha, 4) || !aligned(beta, 4)))
     return HA_ERR_ALIGN;
-  const FmapWs lay = fmap_layout(s, update_state);
+  const FmapWs lay = fmap_layout(s, update_state, false);
   if (workspace_bytes < lay.total) return HA_ERR_WORKSPACE;
 
   const size_t tb = tensor_bytes(s, dtype);
@@ -273,26 +323,94 @@ ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v, 
       overlap(out, tb, wq, wb) || overlap(out, tb, state, stb) || overlap(out, tb, workspace, lay.total) ||
       (update_state && (overlap(out, tb, wk, wb) || overlap(out, tb, wv, wb))))
     return HA_ERR_ALIAS;
+  return fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, (char*)workspace, lay, s, update_state,
+                  resolve_scale(softmax_scale, d), (hipStream_t)stream);
+}
 
-  const float scale = resolve_scale(softmax_scale, d);
-  hipStream_t st = (hipStream_t)stream;
-  const long long dd = (long long)d * d, fb = dd * 2;
+size_t hybrid_attn_gated_workspace_bytes(int B, int H, int T, int frame_len, int d, int update_state) {
+  ha::Shape s;
+  if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK) return 0;
+  return fmap_layout(s, update_state, true).total;
+}
+
+ha_status hybrid_attn_forward_gated(const void* x, const void* q, const void* k, const void* v,
+                                    const void* wq, const void* wk, const void* wv, const void* w_gate,
+                                    const float* b_gate, float* state, void* out, void* workspace,
+                                    size_t workspace_bytes, int B, int H, int T, int d, int C,
+                                    int frame_len, ha_dtype dtype, int update_state, int normalize_k,
+                                    float softmax_scale, void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (dtype != HA_BF16) return HA_ERR_UNSUPPORTED;
+  if (update_state && (r = check_gate_shape(s, C)) != HA_OK) return r;
+  if (!q || !k || !v || !wq || !state || !out || !workspace) return HA_ERR_NULL;
+  if (update_state && (!x || !wk || !wv || !w_gate || !b_gate)) return HA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(wq, 16) ||
+      !aligned(state, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+    return HA_ERR_ALIGN;
+  if (update_state && (!aligned(x, 16) || !aligned(wk, 16) || !aligned(wv, 16) || !aligned(w_gate, 16) ||
+                       !aligned(b_gate, 4)))
+    return HA_ERR_ALIGN;
+  const FmapWs lay = fmap_layout(s, update_state, true);
+  if (workspace_bytes < lay.total) return HA_ERR_WORKSPACE;
+
+  const size_t tb = tensor_bytes(s, dtype);
+  const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
+  const size_t wb = (size_t)H * d * d * 2;
+  const size_t xb = (size_t)B * T * (size_t)(update_state ? C : 0) * 2;
+  const size_t gb = (size_t)2 * H * (size_t)(update_state ? C : 0) * 2;
+  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
+      overlap(out, tb, wq, wb) || overlap(out, tb, state, stb) || overlap(out, tb, workspace, lay.total) ||
+      (update_state && (overlap(out, tb, wk, wb) || overlap(out, tb, wv, wb) || overlap(out, tb, x, xb) ||
+                        overlap(out, tb, w_gate, gb) || overlap(out, tb, b_gate, (size_t)2 * H * 4))))
+    return HA_ERR_ALIAS;
+
   char* ws = (char*)workspace;
-  if (!update_state) {
-    void* mf = ws + lay.mfrag;
-    if (ha::launch_mfrag(state, dd, 0, wq, mf, 1, s, st) != hipSuccess) return HA_ERR_DEVICE;
-    return run_readout(q, k, v, q, nullptr, fb, 0, out, s, dtype, scale, st, mf);
-  }
-  float* gram = (float*)(ws + lay.gram);
-  float* partial = (float*)(ws + lay.partial);
-  float* snaps = (float*)(ws + lay.snaps);
-  void* mf = ws + lay.mfrag;
-  const int nsplit = ha::gram_splits(s);
-  if (ha::launch_gram_partials_bf16(k, v, beta, partial, nsplit, s, st) != hipSuccess) return HA_ERR_DEVICE;
-  if (ha::launch_gram_fmap(partial, nsplit, wk, wv, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
-  if (ha::launch_state_scan_bf16(gram, alpha, state, snaps, nullptr, s, st) != hipSuccess) return HA_ERR_DEVICE;
-  if (ha::launch_mfrag(snaps, (long long)s.F * dd, dd, wq, mf, s.F, s, st) != hipSuccess) return HA_ERR_DEVICE;
-  return run_readout(q, k, v, q, nullptr, (long long)s.F * fb, fb, out, s, dtype, scale, st, mf);
+  hipStream_t st = (hipStream_t)stream;
+  const float scale = resolve_scale(softmax_scale, d);
+  if (!update_state)
+    return fmap_run(q, k, v, wq, wk, wv, nullptr, nullptr, nullptr, state, out, ws, lay, s, 0, scale, st);
+  float* alpha = (float*)(ws + lay.alpha);
+  float* beta = (float*)(ws + lay.beta);
+  if (ha::launch_gates(x, w_gate, b_gate, alpha, beta, (float*)(ws + lay.apart), C, s, st) != hipSuccess)
+    return HA_ERR_DEVICE;
+  if (!normalize_k)
+    return fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, ws, lay, s, 1, scale, st);
+  float* bgv = (float*)(ws + lay.beta_g);
+  float* bbv = (float*)(ws + lay.beta_b);
+  if (ha::launch_keyscale(k, wk, beta, bgv, bbv, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  return fmap_run(q, k, v, wq, wk, wv, alpha, bgv, bbv, state, out, ws, lay, s, 1, scale, st);
+}
+
+size_t hybrid_attn_gates_workspace_bytes(int B, int H, int T, int frame_len) {
+  ha::Shape s;
+  if (check_shape(B, H, T, 64, frame_len, HA_BF16, &s) != HA_OK) return 0;
+  return align_up(ha::gates_partial_bytes(s));
+}
+
+ha_status hybrid_attn_gates(const void* x, const void* w_gate, const float* b_gate, float* alpha, float* beta,
+                            void* workspace, size_t workspace_bytes, int B, int H, int T, int C,
+                            int frame_len, ha_dtype dtype, void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, 64, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (dtype != HA_BF16) return HA_ERR_UNSUPPORTED;
+  if ((r = check_gate_shape(s, C)) != HA_OK) return r;
+  if (!x || !w_gate || !b_gate || !alpha || !beta || !workspace) return HA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(b_gate, 4) || !aligned(alpha, 4) ||
+      !aligned(beta, 4) || !aligned(workspace, 16))
+    return HA_ERR_ALIGN;
+  if (workspace_bytes < align_up(ha::gates_partial_bytes(s))) return HA_ERR_WORKSPACE;
+  const size_t ab = (size_t)B * s.F * H * 4, bb = (size_t)B * T * H * 4;
+  const size_t xb = (size_t)B * T * (size_t)C * 2, gb = (size_t)2 * H * (size_t)C * 2;
+  const size_t wsb = align_up(ha::gates_partial_bytes(s));
+  if (overlap(alpha, ab, beta, bb) || overlap(alpha, ab, x, xb) || overlap(beta, bb, x, xb) ||
+      overlap(alpha, ab, w_gate, gb) || overlap(beta, bb, w_gate, gb) || overlap(alpha, ab, workspace, wsb) ||
+      overlap(beta, bb, workspace, wsb) || overlap(alpha, ab, b_gate, (size_t)2 * H * 4) ||
+      overlap(beta, bb, b_gate, (size_t)2 * H * 4))
+    return HA_ERR_ALIAS;
+  return launched(ha::launch_gates(x, w_gate, b_gate, alpha, beta, (float*)workspace, C, s, (hipStream_t)stream));
 }
 
 }  // extern "C"

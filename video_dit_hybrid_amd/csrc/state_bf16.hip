@@ -65,16 +65,17 @@ constexpr int NT = NW * kWave;
 
 // The increment format and the partial-sum layout: ha_gram_format.h.
 
-template <int D>
+template <int D, bool TWO>
 __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restrict__ kp,
                                                        const uint16_t* __restrict__ vp,
                                                        const float* __restrict__ beta,
+                                                       const float* __restrict__ beta2,
                                                        float* __restrict__ gram,
                                                        float* __restrict__ partial, int nsplit,
                                                        int H, int T, int L, int F) {
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = TC * D * 2;           // bytes of one K' or V' chunk
-  constexpr int BUF = 2 * TILE + TC * 4;     // K', V', beta
+  constexpr int BUF = 2 * TILE + TC * 4 * (TWO ? 2 : 1);  // K', V', beta (and beta2)
   constexpr int SEGS = TILE / 1024;          // 1 KB direct-to-LDS segments per tile
   constexpr int RPS = 64 / NCH;              // rows per segment
   constexpr int NRB = D / 32;                // 32-row (and -column) blocks
@@ -102,8 +103,12 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   const int span = (int)((uint32_t)(L - 1) * rsb + D * 2);
   const u32x4 rk = rsrc_words(kp + fbase, span);
   const u32x4 rv = rsrc_words(vp + fbase, span);
-  const u32x4 rbeta =
-      rsrc_words(beta + ((long long)b * T + (long long)n * L) * H + h, (int)(((uint32_t)(L - 1) * H + 1) * 4));
+  const long long bofs = ((long long)b * T + (long long)n * L) * H + h;
+  const int bspan = (int)(((uint32_t)(L - 1) * H + 1) * 4);
+  const u32x4 rbeta = rsrc_words(beta + bofs, bspan);
+  const u32x4 rbeta2 = rsrc_words((TWO ? beta2 : beta) + bofs, bspan);
+  // waves 0 (and 1 with two step-size vectors) also load the chunk's beta
+  const bool has_beta = wave == 0 || (TWO && wave == 1);
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(smem));
 
   // direct-to-LDS: wave w fills segments w, w + NW, ... of each tile; those are
@@ -121,6 +126,8 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
       dma16_asm(rv, base + TILE + (wave + NW * i) * 1024, soff, so);
     }
     if (wave == 0) dma4_asm(rbeta, base + 2 * TILE, (uint32_t)lane * H * 4, (uint32_t)c * TC * H * 4);
+    if (TWO && wave == 1)
+      dma4_asm(rbeta2, base + 2 * TILE + TC * 4, (uint32_t)lane * H * 4, (uint32_t)c * TC * H * 4);
   };
 
   // transposed-read offsets: 16-lane group g reads rows 8*hh + gi/4 (+4) of a
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
     const int buf = c % NBUF;
     // chunk c landed: at most the loads of the chunks after it are outstanding
     const int later = (nch - 1 - c) < (NBUF - 2) ? (nch - 1 - c) : (NBUF - 2);
-    if (wave == 0) {
+    if (has_beta) {
       if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (2 * MY_SEGS + 1)));
       else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS + 1));
       else __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -168,33 +175,40 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
     const unsigned char* kt = smem + buf * BUF;
     const unsigned char* vt = kt + TILE;
     const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
+    const float* be2 = be + (TWO ? TC : 0);
 #pragma unroll
     for (int kk = 0; kk < KSC / KH; ++kk) {
       const int ks = kh * (KSC / KH) + kk;
       // A = (beta K')^T rows 32*rb.., tokens 16*ks + 8*hh + e: split hi + lo,
-      // shared by the G blocks (B operand K') and the B blocks (B operand V')
+      // shared by the G blocks (B operand K') and the B blocks (B operand V');
+      // with two step-size vectors the B blocks take their own (beta2 K')^T
       const u32x4 kraw = tr8(kt, ks, rb);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(be + 16 * ks + 8 * hh);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(be + 16 * ks + 8 * hh + 4);
-      u32x4 ahi, alo;
+      auto scaled_split = [&](const float* bp, u32x4& hi4, u32x4& lo4) {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh + 4);
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const float bl = w2 < 2 ? b0[2 * w2] : b1[2 * w2 - 4];
-        const float bu = w2 < 2 ? b0[2 * w2 + 1] : b1[2 * w2 - 3];
-        const float x0 = bl * bf16_lo_to_f32(kraw[w2]);
-        const float x1 = bu * bf16_hi_to_f32(kraw[w2]);
-        const uint32_t hi = pack_bf16x2(x0, x1);
-        ahi[w2] = hi;
-        alo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
-      }
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const float bl = w2 < 2 ? b0[2 * w2] : b1[2 * w2 - 4];
+          const float bu = w2 < 2 ? b0[2 * w2 + 1] : b1[2 * w2 - 3];
+          const float x0 = bl * bf16_lo_to_f32(kraw[w2]);
+          const float x1 = bu * bf16_hi_to_f32(kraw[w2]);
+          const uint32_t hi = pack_bf16x2(x0, x1);
+          hi4[w2] = hi;
+          lo4[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+        }
+      };
+      u32x4 ahi, alo, bhi, blo;
+      scaled_split(be, ahi, alo);
+      if constexpr (TWO) scaled_split(be2, bhi, blo);
+      else { bhi = ahi; blo = alo; }
 #pragma unroll
       for (int cb = 0; cb < NRB; ++cb) {
         const u32x4 bk = tr8(kt, ks, cb);
         const u32x4 bv = tr8(vt, ks, cb);
         ag[cb] = mfma32x32x16(ahi, bk, ag[cb]);
-        ab[cb] = mfma32x32x16(ahi, bv, ab[cb]);
+        ab[cb] = mfma32x32x16(bhi, bv, ab[cb]);
         ag[cb] = mfma32x32x16(alo, bk, ag[cb]);
-        ab[cb] = mfma32x32x16(alo, bv, ab[cb]);
+        ab[cb] = mfma32x32x16(blo, bv, ab[cb]);
       }
     }
   }
@@ -300,15 +314,20 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float* beta,
+hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float* beta, const float* beta2,
                                      float* partial, int nsplit, const Shape& s, hipStream_t st) {
   const int grid = (int)((long long)s.B * s.H * s.F * nsplit);
-  if (s.d == 128)
-    gram_bf16_kernel<128><<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, nullptr,
-                                               partial, nsplit, s.H, s.T, s.L, s.F);
-  else
-    gram_bf16_kernel<64><<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, nullptr,
-                                              partial, nsplit, s.H, s.T, s.L, s.F);
+  auto run = [&](auto gk) {
+    gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, beta2, nullptr, partial, nsplit, s.H,
+                            s.T, s.L, s.F);
+  };
+  if (s.d == 128) {
+    if (beta2) run(gram_bf16_kernel<128, true>);
+    else run(gram_bf16_kernel<128, false>);
+  } else {
+    if (beta2) run(gram_bf16_kernel<64, true>);
+    else run(gram_bf16_kernel<64, false>);
+  }
   return hipGetLastError();
 }
 
@@ -320,12 +339,12 @@ hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, f
   float* partial = nsplit > 1 ? gram + gram_final_bytes(s) / sizeof(float) : nullptr;
   const int grid = (int)(groups * nsplit);
   auto run = [&](auto gk, auto rk, int nrb) {
-    gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, gram, partial, nsplit, s.H,
-                            s.T, s.L, s.F);
+    gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, nullptr, gram, partial, nsplit,
+                            s.H, s.T, s.L, s.F);
     if (nsplit > 1) rk<<<(int)(groups * nrb * nrb), 256, 0, st>>>(partial, gram, nsplit, s.H, s.F);
   };
-  if (s.d == 128) run(gram_bf16_kernel<128>, gram_reduce_kernel<128>, 4);
-  else run(gram_bf16_kernel<64>, gram_reduce_kernel<64>, 2);
+  if (s.d == 128) run(gram_bf16_kernel<128, false>, gram_reduce_kernel<128>, 4);
+  else run(gram_bf16_kernel<64, false>, gram_reduce_kernel<64>, 2);
   return hipGetLastError();
 }
 

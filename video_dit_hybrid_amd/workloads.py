@@ -11,6 +11,7 @@ Layouts (token-major, as a fused QKV projection of a DiT emits them):
   alpha               : [B, F, H]      fp32, one forget gate per (stream, frame, head)
   beta                : [B, T, H]      fp32, one step size per (stream, token, head)
   state               : [B, H, d, d]   fp32, S[dk, dv] with dv contiguous
+  x                   : [B, T, C]      the tokens' layer input (C = H * d), for the gates
 
 Every slab is drawn from numpy PCG64 seeded with
 SeedSequence([cfg_id, tensor_id, b, frame, pass]) so that any (stream, frame,
@@ -28,7 +29,8 @@ import numpy as np
 
 # tensor ids used in the seed sequence
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "qp": 3, "kp": 4, "vp": 5,
-              "alpha": 6, "beta": 7, "state": 8, "wq": 9, "wk": 10, "wv": 11}
+              "alpha": 6, "beta": 7, "state": 8, "wq": 9, "wk": 10, "wv": 11,
+              "x": 12, "wgate": 13, "bgate": 14}
 QKV_NAMES = ("q", "k", "v", "qp", "kp", "vp")
 
 
@@ -153,6 +155,39 @@ def make_fmap_weights(w: Workload) -> dict:
         out[name] = _encode(x, w.dtype)
     return out
 
+
+
+def make_gate_weights(w: Workload) -> dict:
+    """Headwise gate projections for the gated variant: wgate [2, H, C]
+    (row 0 alpha, row 1 beta; N(0, 1/sqrt(C)) entries, so that a logit over an
+    N(0, 1) input has unit variance), encoded like the other tensors; bgate
+    [2, H] fp32 = the workload's alpha and beta logit means, so the gates have
+    the plain workload's centres."""
+    C = w.H * w.d
+    g = _rng(w.cfg_id, "wgate", 0, 0, 0)
+    wg = (g.standard_normal((2, w.H, C)) / np.sqrt(C)).astype(np.float32)
+    bg = np.empty((2, w.H), dtype=np.float32)
+    bg[0] = w.alpha_mu
+    bg[1] = w.beta_mu
+    return {"wgate": _encode(wg, w.dtype), "bgate": bg}
+
+
+def make_layer_input(w: Workload, frame0: int, nframes: int, pass_: int, streams=None) -> np.ndarray:
+    """x [nb, nframes * L, C] (C = H * d), N(0, 1) per (stream, frame) slab,
+    encoded to the workload dtype."""
+    streams = list(range(w.B)) if streams is None else list(streams)
+    C = w.H * w.d
+    out = np.empty((len(streams), nframes * w.L, C), dtype=np.uint16 if w.dtype == "bf16" else np.float32)
+
+    def job(args):
+        bi, b, fi = args
+        g = _rng(w.cfg_id, "x", b, frame0 + fi, pass_)
+        out[bi, fi * w.L:(fi + 1) * w.L] = _encode(g.standard_normal((w.L, C), dtype=np.float32), w.dtype)
+
+    jobs = [(bi, b, fi) for bi, b in enumerate(streams) for fi in range(nframes)]
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, jobs))
+    return out
 
 def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
