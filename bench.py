@@ -2,6 +2,11 @@
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 480p] [--no-cpu]
 
+Variants (not the headline line): --variant fmap (per-head feature maps
+applied inside the call) and --variant gated (gates projected from the layer
+input x, maps, L2-normalised K'), each against the same prologue done by
+separate torch ops before hybrid_attn_forward.
+
 Other workloads (not the headline line): --workload 720p (one clean call,
 H=40, 21 x 3600 tokens); --workload stream (120 frames, each 4 query-only
 denoise calls + 1 clean call, F=1 per call; frames/s over all 600 calls);
@@ -201,6 +206,126 @@ def bench_streaming(w, args):
     print(json.dumps(res), flush=True)
 
 
+
+def bench_variant(w, args):
+    """The layer with its prologue inside the call: --variant fmap (per-head
+    feature maps, alpha and beta given) or --variant gated (alpha and beta
+    projected from the layer input x [B, T, C = H d], maps, L2-normalised K'),
+    against the same prologue done by separate torch ops (per-head bmm maps,
+    normalisation, gate matmul + sigmoid + frame mean) followed by
+    hybrid_attn_forward. One clean call over the whole workload per step."""
+    import torch
+    from video_dit_hybrid_amd import api
+    from video_dit_hybrid_amd import workloads as W
+    dev = torch.device("cuda:0")
+    B, T, H, d, L, F = w.B, w.T, w.H, w.d, w.L, w.frames
+    C = H * d
+    gated = args.variant == "gated"
+    log(f"bench: {args.variant} variant, workload {w.name}: generating inputs")
+    names = ["q", "k", "v"] + ([] if gated else ["alpha", "beta"])
+    inp = W.make_call_inputs(w, 0, F, 0, tensors=names)
+    t = {k: W.as_torch(v, "bf16" if k in W.QKV_NAMES else "fp32", dev) for k, v in inp.items()}
+    mw = {k: W.as_torch(v, "bf16", dev) for k, v in W.make_fmap_weights(w).items()}
+    if gated:
+        x = W.as_torch(W.make_layer_input(w, 0, F, 0), "bf16", dev)
+        g = W.make_gate_weights(w)
+        wg, bg = W.as_torch(g["wgate"], "bf16", dev), W.as_torch(g["bgate"], "fp32", dev)
+    s0 = torch.from_numpy(W.make_state0(w)).to(dev)
+    state = s0.clone()
+    out = torch.empty_like(t["q"])
+    need = (api.gated_workspace_bytes if gated else api.fmap_workspace_bytes)(B, H, T, L, d, 1)
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+
+    def fused():
+        if gated:
+            api.hybrid_attn_forward_gated(x, t["q"], t["k"], t["v"], mw["wq"], mw["wk"], mw["wv"], wg, bg, state,
+                                          L, 1, normalize_k=True, out=out, workspace=ws)
+        else:
+            api.hybrid_attn_forward_fmap(t["q"], t["k"], t["v"], mw["wq"], mw["wk"], mw["wv"], t["alpha"],
+                                         t["beta"], state, L, 1, out=out, workspace=ws)
+
+    out2 = torch.empty_like(out)
+    ws2 = torch.empty(max(1, api.workspace_bytes(B, H, T, L, d, 1)), dtype=torch.uint8, device=dev)
+
+    def per_head_map(a, wm):  # [B, T, H, d] x [H, d, d] -> [B, T, H, d], contiguous bmm operands
+        ah = a.reshape(B * T, H, d).transpose(0, 1).contiguous()
+        return torch.bmm(ah, wm).transpose(0, 1).contiguous().view(B, T, H, d)
+
+    def unfused(st):
+        qp = per_head_map(t["q"], mw["wq"])
+        kp = per_head_map(t["k"], mw["wk"])
+        vp = per_head_map(t["v"], mw["wv"])
+        if gated:
+            kf = kp.float()
+            kp = (kf / kf.norm(dim=-1, keepdim=True).clamp_min(1e-12)).to(torch.bfloat16)
+            z = torch.mm(x.view(B * T, C), wg.view(2 * H, C).t().contiguous()).float() + bg.view(1, 2 * H)
+            sg = torch.sigmoid(z)
+            alpha = sg[:, :H].reshape(B, F, L, H).mean(dim=2).contiguous()
+            beta = (sg[:, H:] / L).reshape(B, T, H).contiguous()
+        else:
+            alpha, beta = t["alpha"], t["beta"]
+        api.hybrid_attn_forward(t["q"], t["k"], t["v"], qp, kp, vp, alpha, beta, st, L, 1, out=out2,
+                                workspace=ws2)
+
+    # one call of each from S_0: their outputs agree up to the rounding of the
+    # materialised Q', K', V' to bf16
+    fused()
+    st_u = s0.clone()
+    unfused(st_u)
+    torch.cuda.synchronize()
+    diff_out = float((out.float() - out2.float()).abs().max() / out2.float().abs().max())
+    diff_state = float((state - st_u).abs().max() / st_u.abs().max())
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    log(f"bench: warmup {args.warmup}, timed {args.steps}")
+    ms = timed(fused)
+    ms_u = timed(lambda: unfused(st_u))
+    res = {"metric": f"hybrid-attn frames/sec, {w.name} workload, {args.variant} layer "
+                     f"({'gates from x + per-head maps + normalised K' if gated else 'per-head maps'} "
+                     "inside the call), 1 MI355X",
+           "value": round(B * F / (ms / 1e3), 1), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{w.name} hybrid attention layer, {args.variant} variant", "B": B, "H": H, "d": d,
+                      "frames": F, "frame_len": L, "tokens": T, **({"C": C} if gated else {}), "update_state": 1},
+           "unfused": {"ms_per_step": round(ms_u, 4), "value": round(B * F / (ms_u / 1e3), 1),
+                       "prologue": "torch: per-head bmm maps" + (", K' normalisation, gate mm + sigmoid + frame "
+                                                                  "mean" if gated else "") +
+                                   ", then hybrid_attn_forward"},
+           "speedup_vs_unfused": round(ms_u / ms, 3),
+           "fused_vs_unfused": {"out_rel_diff": diff_out, "state_rel_diff": diff_state}}
+    if gated:
+        # the gate pass alone, timed with HIP events on its stream: HBM-bound on x
+        stream = torch.cuda.current_stream(dev)
+        al = torch.empty((B, F, H), dtype=torch.float32, device=dev)
+        be = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+        gws = torch.empty(max(1, api.gates_workspace_bytes(B, H, T, L)), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            api.hybrid_attn_gates(x, wg, bg, H, L, alpha=al, beta=be, workspace=gws)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            api.hybrid_attn_gates(x, wg, bg, H, L, alpha=al, beta=be, workspace=gws)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        gms = ev[0].elapsed_time(ev[1]) / args.steps
+        gbytes = B * T * C * 2 + 2 * H * C * 2 + 2 * H * 4 + B * T * H * 4 + B * F * H * 4
+        res["gates_roofline"] = {"bound": "hbm", "achieved": round(gbytes / (gms / 1e3) / 1e9, 1),
+                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(gbytes / (gms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                                 "kernel": "gates_kernel + alpha_kernel (hybrid_attn_gates)",
+                                 "bytes_per_launch": gbytes, "avg_launch_ms": round(gms, 4)}
+    print(json.dumps(res), flush=True)
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +334,9 @@ def main():
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "tiny", "stream", "batched"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--variant", choices=["plain", "fmap", "gated"], default="plain",
+                    help="plain: the layer on given Q', K', V', alpha, beta (the headline); fmap / gated: the "
+                         "prologue (maps; gates from x) inside the call, against an unfused torch prologue")
     ap.add_argument("--kernel", choices=["attn", "update", "copy"], default=None,
                     help="launch only one phase (readout-only attention, or the state update) "
                          "steps times, for profilers; prints its average time")
@@ -223,6 +351,12 @@ def main():
     from video_dit_hybrid_amd import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.variant != "plain":
+        if w.frames_per_call or w.dtype != "bf16":
+            print("--variant runs one bf16 clean call over a whole workload (480p, 720p)", file=sys.stderr)
+            sys.exit(2)
+        bench_variant(w, args)
+        return
     if w.frames_per_call:
         bench_streaming(w, args)
         return
