@@ -215,7 +215,7 @@ ha_status hybrid_attn_forward_gated(const void* x, const void* q, const void* k,
 
 /*
  * Bytes of workspace hybrid_attn_gates needs (the per-chunk alpha sums,
- * B * F * ceil(L / 32) * H floats, 256-byte aligned). 0 for invalid sizes.
+ * B * F * ceil(L / 64) * H floats, 256-byte aligned). 0 for invalid sizes.
  */
 size_t hybrid_attn_gates_workspace_bytes(int B, int H, int T, int frame_len);
 

@@ -125,12 +125,12 @@ def test_feature_map_and_gated_workspace_sizes():
     fmap1 = up(gf) + up(gf) + up(H * F * d * d * 4) + up(H * F * d * d * 2)
     assert api.fmap_workspace_bytes(1, H, T, L, d, 0) == up(H * d * d * 2)
     assert api.fmap_workspace_bytes(1, H, T, L, d, 1) == fmap1
-    # gated: beta, beta / n^2, beta / n, per-32-token-chunk alpha sums (49 chunks
+    # gated: beta, beta / n^2, beta / n, per-64-token-chunk alpha sums (25 chunks
     # of a 1560-token frame), alpha
     tok = up(T * H * 4)
-    assert api.gated_workspace_bytes(1, H, T, L, d, 1) == fmap1 + 3 * tok + up(F * 49 * H * 4) + up(F * H * 4)
+    assert api.gated_workspace_bytes(1, H, T, L, d, 1) == fmap1 + 3 * tok + up(F * 25 * H * 4) + up(F * H * 4)
     assert api.gated_workspace_bytes(1, H, T, L, d, 0) == api.fmap_workspace_bytes(1, H, T, L, d, 0)
-    assert api.gates_workspace_bytes(1, H, T, L) == up(F * 49 * H * 4)
+    assert api.gates_workspace_bytes(1, H, T, L) == up(F * 25 * H * 4)
     assert api.gated_workspace_bytes(1, H, T + 1, L, d, 1) == 0
 
 

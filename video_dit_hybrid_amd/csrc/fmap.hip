@@ -265,10 +265,11 @@ __global__ __launch_bounds__(D / 32 * 64) void mfrag_kernel(const float* __restr
 // and K'^T diag(beta) V' = W_k^T (K^T diag(beta / n) V) W_v, so the increment
 // pass keeps the unmapped K, V and takes two step-size vectors. This kernel
 // writes them: beta_g = beta / n^2, beta_b = beta / n.
-// One work-group (4 waves) per (b, 256-token chunk, head h): W_k of head h is
-// staged in LDS; wave w computes Y^T = W_k^T K^T for 64 tokens (two 32-token
-// column blocks; A = W_k^T by transposed LDS reads, B = K^T straight from the
-// token-major K rows), and n_t^2 is the column sum of squares of Y^T: its own
+// One work-group (4 waves) per (b, 512-token chunk, head h): W_k of head h is
+// staged in LDS; wave w computes Y^T = W_k^T K^T for 128 tokens, one 32-token
+// column block at a time (A = W_k^T by transposed LDS reads, B = K^T straight
+// from the token-major K rows, the next block's rows loaded while the current
+// one computes), and n_t^2 is the column sum of squares of Y^T: its own
 // registers, then the other half-wave.
 template <int D>
 __global__ __launch_bounds__(256) void keyscale_kernel(const uint16_t* __restrict__ k,
@@ -276,43 +277,56 @@ __global__ __launch_bounds__(256) void keyscale_kernel(const uint16_t* __restric
                                                        const float* __restrict__ beta,
                                                        float* __restrict__ beta_g, float* __restrict__ beta_b,
                                                        int H, int T, int nchunk) {
-  constexpr int NRB = D / 32, KS = D / 16;
+  constexpr int NRB = D / 32, KS = D / 16, NTB = 4;  // 4 column blocks of 32 tokens per wave
   __shared__ __align__(16) unsigned char wl[D * D * 2];
   const int blk = blockIdx.x;
   const int h = blk % H, rest = blk / H;
   const int ch = rest % nchunk, b = rest / nchunk;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  stage_w<D>(wl, wk + (size_t)h * D * D, tid, 256);
-  __syncthreads();
-#pragma unroll 1
-  for (int tb = 0; tb < 2; ++tb) {
-    const int t = ch * 256 + w * 64 + tb * 32 + lr;
+  const int t0 = ch * (4 * NTB * 32) + w * (NTB * 32) + lr;
+  auto load = [&](int tb, u32x4* kb) {
+    const int t = t0 + 32 * tb;
     const uint16_t* kr = k + (((size_t)b * T + (t < T ? t : T - 1)) * H + h) * D;
-    f32x16 acc[NRB];
-#pragma unroll
-    for (int eb = 0; eb < NRB; ++eb) acc[eb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c0 = 16 * ks + 4 * hh;
       const u32x2 k0 = *reinterpret_cast<const u32x2*>(kr + c0);
       const u32x2 k1 = *reinterpret_cast<const u32x2*>(kr + c0 + 8);
-      const u32x4 kb = u32x4{k0[0], k0[1], k1[0], k1[1]};
-#pragma unroll
-      for (int eb = 0; eb < NRB; ++eb) acc[eb] = mfma32x32x16(wtr<D>(wl, ks, eb, lane), kb, acc[eb]);
+      kb[ks] = u32x4{k0[0], k0[1], k1[0], k1[1]};
     }
+  };
+  u32x4 cur[KS], nxt[KS];
+  load(0, cur);
+  stage_w<D>(wl, wk + (size_t)h * D * D, tid, 256);
+  __syncthreads();
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    if (tb + 1 < NTB) load(tb + 1, nxt);
+    f32x16 acc[NRB];
+#pragma unroll
+    for (int eb = 0; eb < NRB; ++eb) acc[eb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int eb = 0; eb < NRB; ++eb) acc[eb] = mfma32x32x16(wtr<D>(wl, ks, eb, lane), cur[ks], acc[eb]);
     float ss = 0.0f;
 #pragma unroll
     for (int eb = 0; eb < NRB; ++eb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ss = fmaf(acc[eb][r], acc[eb][r], ss);
     ss += __shfl_xor(ss, 32);
+    const int t = t0 + 32 * tb;
     if (hh == 0 && t < T) {
       const float n2 = fmaxf(ss, 1e-24f);
       const size_t i = ((size_t)b * T + t) * H + h;
       const float be = beta[i];
       beta_g[i] = be / n2;
       beta_b[i] = be / sqrtf(n2);
+    }
+    if (tb + 1 < NTB) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
     }
   }
 }
@@ -344,7 +358,7 @@ hipError_t launch_mfrag(const float* states, long long sbh, long long sfr, const
 
 hipError_t launch_keyscale(const void* k, const void* wk, const float* beta, float* beta_g, float* beta_b,
                            const Shape& s, hipStream_t st) {
-  const int nchunk = (s.T + 255) / 256;
+  const int nchunk = (s.T + 511) / 512;
   const int grid = s.B * nchunk * s.H;
   if (s.d == 128)
     keyscale_kernel<128><<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)wk, beta, beta_g, beta_b, s.H,

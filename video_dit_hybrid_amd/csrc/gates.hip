@@ -18,20 +18,22 @@
 namespace ha {
 namespace {
 
-constexpr int GT = 32;  // tokens per work-group
+constexpr int GT = 64;  // tokens per work-group
 
-// One work-group (4 waves) per (b, frame, 32-token chunk of the frame). Wave w
-// takes the k-steps ks = w, w + 4, ... of the C / 16; the four partial logit
-// blocks are added through LDS in wave order. Outputs: beta for the chunk's
-// tokens, and the chunk's sum of alpha gates per head (apart, summed over the
-// chunks of a frame by alpha_kernel in chunk order).
+// One work-group (4 waves) per (b, frame, 64-token chunk of the frame). Wave w
+// takes the k-steps ks = w, w + 4, ... of the C / 16 for both 32-token column
+// blocks, so each gate-weight fragment it loads serves 64 tokens; the four
+// partial logit blocks are added through LDS in wave order. Outputs: beta for
+// the chunk's tokens, and the chunk's sum of alpha gates per head (apart,
+// added up per frame by alpha_kernel).
 template <int NOB>
 __global__ __launch_bounds__(256) void gates_kernel(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ wg,
                                                     const float* __restrict__ bg, float* __restrict__ beta,
                                                     float* __restrict__ apart, int T, int C, int H, int L,
                                                     int F, int nch) {
-  __shared__ float red[4][NOB][16][64];
+  constexpr int UNR = NOB <= 2 ? 8 : 4;  // k-steps whose loads are issued together
+  __shared__ float red[4][NOB][2][16][64];
   __shared__ float sa[16 * NOB][GT];
   const int blk = blockIdx.x;
   const int c = blk % nch, bn = blk / nch;
@@ -40,52 +42,63 @@ __global__ __launch_bounds__(256) void gates_kernel(const uint16_t* __restrict__
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int O = 2 * H;
 
-  const int tok = c * GT + lr;  // token within the frame; the tail reads the last one
-  const uint16_t* xr = x + ((size_t)b * T + (size_t)n * L + (tok < L ? tok : L - 1)) * C + 8 * hh;
+  // token rows of the two column blocks; the tail reads the frame's last token
+  const uint16_t* xr[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int tok = c * GT + 32 * tb + lr;
+    xr[tb] = x + ((size_t)b * T + (size_t)n * L + (tok < L ? tok : L - 1)) * C + 8 * hh;
+  }
   const uint16_t* wr[NOB];
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) {
     const int o = 32 * ob + lr;  // rows past 2H repeat the last one; never stored
     wr[ob] = wg + (size_t)(o < O ? o : O - 1) * C + 8 * hh;
   }
-  f32x16 acc[NOB];
+  f32x16 acc[NOB][2];
 #pragma unroll
-  for (int ob = 0; ob < NOB; ++ob) acc[ob] = f32x16{};
+  for (int ob = 0; ob < NOB; ++ob) acc[ob][0] = acc[ob][1] = f32x16{};
   const int nks = C / 16;
-  for (int ks0 = w; ks0 < nks; ks0 += 32) {
-    u32x4 xb[8], wa[8][NOB];
+  for (int ks0 = w; ks0 < nks; ks0 += 4 * UNR) {
+    u32x4 xb[UNR][2], wa[UNR][NOB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < UNR; ++i) {
       const int ks = ks0 + 4 * i;
       if (ks < nks) {
-        xb[i] = ld_global_16B(xr + 16 * ks);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) xb[i][tb] = ld_global_16B(xr[tb] + 16 * ks);
 #pragma unroll
         for (int ob = 0; ob < NOB; ++ob) wa[i][ob] = ld_global_16B(wr[ob] + 16 * ks);
       } else {
-        xb[i] = u32x4{0, 0, 0, 0};
+        xb[i][0] = xb[i][1] = u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int ob = 0; ob < NOB; ++ob) wa[i][ob] = u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < UNR; ++i)
 #pragma unroll
-      for (int ob = 0; ob < NOB; ++ob) acc[ob] = mfma32x32x16(wa[i][ob], xb[i], acc[ob]);
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[ob][tb] = mfma32x32x16(wa[i][ob], xb[i][tb], acc[ob][tb]);
   }
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[w][ob][r][lane] = acc[ob][r];
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[w][ob][tb][r][lane] = acc[ob][tb][r];
   __syncthreads();
 
-  // logit (o, t) sits in register r = 4*(oo/8) + oo%4 of lane t + 32*((oo/4)%2),
-  // oo = o % 32, of block o / 32
+  // logit (o, t) sits in register r = 4*(oo/8) + oo%4 of lane t%32 + 32*((oo/4)%2)
+  // of block (o / 32, t / 32), oo = o % 32
   for (int idx = tid; idx < O * GT; idx += 256) {
     const int o = idx / GT, t = idx % GT;
-    const int ob = o >> 5, oo = o & 31;
+    const int ob = o >> 5, oo = o & 31, tb = t >> 5;
     const int r = ((oo >> 3) << 2) | (oo & 3);
-    const int ln = t + 32 * ((oo >> 2) & 1);
-    const float z = red[0][ob][r][ln] + red[1][ob][r][ln] + red[2][ob][r][ln] + red[3][ob][r][ln] + bg[o];
+    const int ln = (t & 31) + 32 * ((oo >> 2) & 1);
+    const float z = red[0][ob][tb][r][ln] + red[1][ob][tb][r][ln] + red[2][ob][tb][r][ln] +
+                    red[3][ob][tb][r][ln] + bg[o];
     const float gsig = 1.0f / (1.0f + expf(-z));
     const bool valid = c * GT + t < L;
     if (o >= H) {
@@ -97,21 +110,25 @@ __global__ __launch_bounds__(256) void gates_kernel(const uint16_t* __restrict__
   __syncthreads();
   for (int h = tid; h < H; h += 256) {
     float s = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
     for (int t = 0; t < GT; ++t) s += sa[h][t];
     apart[((size_t)bn * nch + c) * H + h] = s;
   }
 }
 
-// alpha[b, n, h] = (sum over the frame's chunks, in chunk order) / L
+// alpha[b, n, h] = (sum of the frame's chunk sums) / L: one wave per (b, n, h),
+// lane l adds chunks l, l + 64, ... and a butterfly over the 64 lanes adds
+// those (an order fixed by the shape).
 __global__ __launch_bounds__(256) void alpha_kernel(const float* __restrict__ apart, float* __restrict__ alpha,
                                                     int nch, int H, int total, int L) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const int bn = i / H, h = i % H;
+  const int wv = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wv >= total) return;
+  const int bn = wv / H, h = wv % H;
   float s = 0.0f;
-  for (int c = 0; c < nch; ++c) s += apart[((size_t)bn * nch + c) * H + h];
-  alpha[i] = s / (float)L;
+  for (int c = lane; c < nch; c += 64) s += apart[((size_t)bn * nch + c) * H + h];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) alpha[wv] = s / (float)L;
 }
 
 }  // namespace
@@ -139,7 +156,7 @@ hipError_t launch_gates(const void* x, const void* wg, const float* bg, float* a
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = s.B * s.F * s.H;
-  alpha_kernel<<<(total + 255) / 256, 256, 0, st>>>(apart, alpha, nch, s.H, total, s.L);
+  alpha_kernel<<<(total + 3) / 4, 256, 0, st>>>(apart, alpha, nch, s.H, total, s.L);
   return hipGetLastError();
 }
 
