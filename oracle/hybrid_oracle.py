@@ -40,6 +40,12 @@ Readings where the page is silent or garbled (each is listed in the design doc):
     the frame's alpha_N is the mean of its tokens' alpha gates (one write per
     frame), and beta_t is the token's gate divided by the frame length L.
 
+The softmax teacher the hybrid layer replaces (ARL2 section 1: chunk-wise
+causal attention with a KV cache that grows with every generated chunk;
+section 4: the baselines' memory and time grow with video length) is here too
+(chunk_causal_attention): the queries of frame N attend to the keys of frames
+0..N, bidirectionally inside frame N.
+
 Every function here is pinned by tests/test_oracle_pins.py against
 properties the page and the mathematics fix (row sums, closed forms, the
 delta-rule recall property, brute force on tiny inputs, textbook attention).
@@ -233,3 +239,22 @@ def hybrid_layer_gated(x, q, k, v, wq, wk, wv, w_gate, b_gate, state, frame_len,
     qp, kp, vp = feature_maps(q, k, v, wq, wk, wv, normalize_k)
     out, st = hybrid_layer(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale)
     return out, st, alpha, beta
+
+
+def chunk_causal_attention(q, k, v, frame_len, scale=None):
+    """Softmax attention with a full KV cache, one head (the teacher of ARL2
+    section 1: chunk-wise causal generation, every chunk attending to the keys
+    and values of all chunks generated so far and to its own).
+
+    q, k, v: [T, d] fp64, T = F * L. Frame N's queries (rows [N L, (N+1) L))
+    attend to keys [0, (N+1) L): no mask inside the frame, none of the later
+    frames. Returns [T, d].
+    """
+    T = q.shape[0]
+    L = int(frame_len)
+    out = np.empty((T, v.shape[1]), dtype=np.float64)
+    for n in range(T // L):
+        r = slice(n * L, (n + 1) * L)
+        vis = slice(0, (n + 1) * L)
+        out[r] = intra_frame_attention(q[r], k[vis], v[vis], scale)
+    return out

@@ -525,7 +525,80 @@ def check_gated_fold_normalised(o):
     assert np.allclose(st2, st, rtol=1e-11, atol=1e-13)
 
 
+
+# --- the KV-cache softmax teacher ---------------------------------------------
+
+def check_chunk_causal_single_frame(o):
+    """One frame: chunk-causal attention is the frame's own softmax attention."""
+    rng = np.random.default_rng(41)
+    q, k, v = (rng.standard_normal((8, 4)) for _ in range(3))
+    assert np.allclose(o.chunk_causal_attention(q, k, v, 8), o.intra_frame_attention(q, k, v),
+                       rtol=1e-14, atol=1e-15)
+
+
+def check_chunk_causal_is_block_masked_sdpa(o):
+    """Against torch's fp64 scaled_dot_product_attention with an explicit
+    block mask: key j is visible to query i iff frame(j) <= frame(i); and the
+    last frame sees every key (the unmasked routine)."""
+    import torch
+    rng = np.random.default_rng(42)
+    T, d, L = 12, 5, 4
+    q, k, v = (rng.standard_normal((T, d)) for _ in range(3))
+    got = o.chunk_causal_attention(q, k, v, L)
+    fr = np.arange(T) // L
+    mask = torch.from_numpy(fr[None, :] <= fr[:, None])
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)[0, 0].numpy()
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-13)
+    full = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, 0].numpy()
+    assert np.allclose(got[8:], full[8:], rtol=1e-12, atol=1e-13)
+
+
+def check_chunk_causal_brute_force(o):
+    """Scalar loops: softmax over keys of frames <= the query's frame."""
+    rng = np.random.default_rng(43)
+    T, d, L = 6, 3, 2
+    q, k, v = (rng.standard_normal((T, d)) for _ in range(3))
+    sc = 0.7
+    got = o.chunk_causal_attention(q, k, v, L, sc)
+    for i in range(T):
+        vis = range(0, (i // L + 1) * L)
+        z = [sum(q[i, c] * k[j, c] for c in range(d)) * sc for j in vis]
+        m = max(z)
+        e = [math.exp(x - m) for x in z]
+        den = sum(e)
+        for c in range(d):
+            want = sum(e[t] * v[j, c] for t, j in enumerate(vis)) / den
+            assert abs(got[i, c] - want) < 1e-13
+
+
+def check_chunk_causal_causality_and_streaming(o):
+    """Perturbing frame m leaves the outputs of frames < m and changes those of
+    frames >= m; frame by frame over a growing cache (each frame's queries on
+    the keys of the frames so far) equals the whole call; the order of the
+    visible past tokens does not matter (attention over a set)."""
+    rng = np.random.default_rng(44)
+    T, d, L = 16, 4, 4
+    q, k, v = (rng.standard_normal((T, d)) for _ in range(3))
+    out = o.chunk_causal_attention(q, k, v, L)
+    k2, v2 = k.copy(), v.copy()
+    k2[8:12] += 1.0
+    v2[8:12] -= 0.5
+    out2 = o.chunk_causal_attention(q, k2, v2, L)
+    assert np.array_equal(out2[:8], out[:8]) and not np.allclose(out2[8:], out[8:])
+    for n in range(4):
+        step = o.intra_frame_attention(q[n * L:(n + 1) * L], k[:(n + 1) * L], v[:(n + 1) * L])
+        assert np.allclose(step, out[n * L:(n + 1) * L], rtol=1e-14, atol=1e-15)
+    perm = np.concatenate([rng.permutation(12), np.arange(12, 16)])
+    last = o.intra_frame_attention(q[12:], k[perm], v[perm])
+    assert np.allclose(last, out[12:], rtol=1e-13, atol=1e-14)
+
+
 ALL_CHECKS = [
+    check_chunk_causal_single_frame,
+    check_chunk_causal_is_block_masked_sdpa,
+    check_chunk_causal_brute_force,
+    check_chunk_causal_causality_and_streaming,
     check_gates_brute_force,
     check_gates_zero_projection,
     check_gates_constant_frame,

@@ -193,7 +193,29 @@ def m_normalise_q_too(m):
     m.feature_maps = f
 
 
+
+def _causal_variant(m, lo=None, hi=None, token_causal=False):
+    def f(q, k, v, frame_len, scale=None):
+        T, L = q.shape[0], int(frame_len)
+        out = np.empty_like(v, dtype=np.float64)
+        for n in range(T // L):
+            r = slice(n * L, (n + 1) * L)
+            a = 0 if lo is None else lo(n, L)
+            b = (n + 1) * L if hi is None else min(T, hi(n, L))
+            if token_causal:
+                for i in range(n * L, (n + 1) * L):
+                    out[i] = m.intra_frame_attention(q[i:i + 1], k[a:i + 1], v[a:i + 1], scale)[0]
+            else:
+                out[r] = m.intra_frame_attention(q[r], k[a:b], v[a:b], scale)
+        return out
+    m.chunk_causal_attention = f
+
+
 MUTANTS = {
+    "causal_sees_next_frame": lambda m: _causal_variant(m, hi=lambda n, L: (n + 2) * L),
+    "causal_misses_own_frame": lambda m: _causal_variant(m, hi=lambda n, L: max(n, 1) * L),
+    "causal_own_frame_only": lambda m: _causal_variant(m, lo=lambda n, L: n * L),
+    "causal_token_mask_in_frame": lambda m: _causal_variant(m, token_causal=True),
     "gates_swapped": m_gates_swapped,
     "beta_not_over_frame_len": m_beta_not_over_frame_len,
     "alpha_first_token": m_alpha_first_token,
