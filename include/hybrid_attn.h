@@ -232,6 +232,44 @@ ha_status hybrid_attn_gates(const void* x, const void* w_gate, const float* b_ga
                             int B, int H, int T, int C, int frame_len, ha_dtype dtype,
                             void* stream);
 
+/*
+ * Bytes of workspace hybrid_attn_kvcache_forward needs for these sizes and
+ * frame_index: 0 when every (b, h, frame) runs in one work-group set;
+ * otherwise room for the key splits' fp32 partial outputs (nsplit x B x T x
+ * H x d floats) and their (max, sum) pairs (nsplit x B x T x H x 8 bytes),
+ * 256-byte aligned. The split count depends on the sizes only (few query
+ * work-groups, long caches). Returns 0 also for invalid sizes.
+ */
+size_t hybrid_attn_kvcache_workspace_bytes(int B, int H, int T, int frame_len, int d, int frame_index);
+
+/*
+ * The softmax attention the hybrid layer replaces, with a full KV cache
+ * (ARL2 section 1: chunk-wise causal generation; every generated chunk keeps
+ * its keys and values for all later chunks, so memory and time grow with the
+ * video). For the call's F = T / frame_len frames, which are frames
+ * frame_index .. frame_index + F - 1 of the video:
+ *   1. k, v are written into the cache at frames frame_index .. + F - 1
+ *      (a later call for the same frames overwrites them: denoising passes
+ *      leave their own K, V there until the clean pass replaces them);
+ *   2. the queries of call frame n attend, with one softmax, to the cache's
+ *      keys of frames 0 .. frame_index + n (bidirectional inside their frame,
+ *      no later frame); out = softmax(Q K^T * s) V, no readout, no state.
+ *   q, k, v, out   [B, T, H, d] bf16
+ *   k_cache, v_cache [B, cache_frames * frame_len, H, d] bf16, caller-owned;
+ *                  frames < frame_index must hold the earlier frames' K, V
+ *   workspace      hybrid_attn_kvcache_workspace_bytes(...) bytes (may be
+ *                  NULL when that is 0)
+ * bf16 only. HA_ERR_SHAPE if frame_index + F > cache_frames; HA_ERR_ALIAS if
+ * out overlaps an input, the caches or the workspace, or k, v, q overlap a
+ * cache. Other errors and stream behaviour as for hybrid_attn_forward.
+ */
+ha_status hybrid_attn_kvcache_forward(const void* q, const void* k, const void* v,
+                                      void* k_cache, void* v_cache, void* out,
+                                      void* workspace, size_t workspace_bytes,
+                                      int B, int H, int T, int d, int frame_len,
+                                      int cache_frames, int frame_index, ha_dtype dtype,
+                                      float softmax_scale, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* hybrid_attn_status_string(int status);
 

@@ -178,3 +178,30 @@ def test_gates_entry_validates():
     assert g(x=4097) == 4
     assert g(wsb=4) == 5
     assert g(be=16384 + 8) == 7
+
+
+def test_kvcache_workspace_and_validation():
+    up = lambda x: (x + 255) // 256 * 256
+    L, H, d = 1560, 12, 128
+    # one frame against a cache of 1 frame: 156 query work-groups, 25 key tiles: no split
+    assert api.kvcache_workspace_bytes(1, H, L, L, d, 0) == 0
+    # at frame 20: 512 key tiles, ceil(512 / 156) = 4 splits
+    rows = L * H
+    assert api.kvcache_workspace_bytes(1, H, L, L, d, 20) == up(4 * rows * d * 4) + up(4 * rows * 8)
+    # a 21-frame call has 3276 query work-groups: no split
+    assert api.kvcache_workspace_bytes(1, H, 21 * L, L, d, 0) == 0
+    assert api.kvcache_workspace_bytes(1, H, L + 1, L, d, 0) == 0
+
+    def kv(q=4096, k=8192, v=12288, kc=1 << 30, vc=1 << 31, out=1 << 32, ws=None, wsb=0, B=1, H=2, T=64, d=64,
+           L=32, cap=4, fi=0, dtype=0):
+        p = lambda x: None if x is None else P(x)
+        return api.lib().hybrid_attn_kvcache_forward(p(q), p(k), p(v), p(kc), p(vc), p(out), p(ws), wsb, B, H, T,
+                                                     d, L, cap, fi, dtype, 0.0, None)
+    assert kv(fi=3) == 2 and kv(cap=1) == 2 and kv(fi=-1) == 2
+    assert kv(q=None) == 1 and kv(kc=None) == 1
+    assert kv(dtype=1) == 3 and kv(d=96) == 3
+    assert kv(k=8200) == 4
+    assert kv(out=(1 << 30) + 64) == 7 and kv(k=(1 << 31) + 64) == 7
+    # a long cache with one frame of queries needs split workspace
+    assert kv(T=1560, L=1560, H=12, d=128, cap=40, fi=30, q=1 << 33, k=1 << 34, v=1 << 35, kc=1 << 36,
+              vc=1 << 37, out=1 << 38) == 5

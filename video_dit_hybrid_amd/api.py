@@ -17,7 +17,8 @@ EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_in
            "hybrid_attn_state_update", "hybrid_attn_state_workspace_bytes",
            "hybrid_attn_status_string", "hybrid_attn_version", "hybrid_attn_forward_fmap",
            "hybrid_attn_fmap_workspace_bytes", "hybrid_attn_forward_gated",
-           "hybrid_attn_gated_workspace_bytes", "hybrid_attn_gates", "hybrid_attn_gates_workspace_bytes")
+           "hybrid_attn_gated_workspace_bytes", "hybrid_attn_gates", "hybrid_attn_gates_workspace_bytes",
+           "hybrid_attn_kvcache_forward", "hybrid_attn_kvcache_workspace_bytes")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_attn.so")
 _lib = None
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.hybrid_attn_gates.restype = i
     L.hybrid_attn_gates_workspace_bytes.argtypes = [i, i, i, i]
     L.hybrid_attn_gates_workspace_bytes.restype = sz
+    L.hybrid_attn_kvcache_forward.argtypes = [vp] * 7 + [sz, i, i, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_kvcache_forward.restype = i
+    L.hybrid_attn_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.hybrid_attn_kvcache_workspace_bytes.restype = sz
     L.hybrid_attn_status_string.argtypes = [i]
     L.hybrid_attn_status_string.restype = ctypes.c_char_p
     L.hybrid_attn_version.argtypes = []
@@ -284,6 +289,47 @@ def hybrid_attn_forward_gated(x, q, k, v, wq, wk, wv, w_gate, b_gate, state, fra
         code, int(u), int(bool(normalize_k)), float(softmax_scale), _stream(dev))
     if st != 0:
         raise HybridAttnError(st, "hybrid_attn_forward_gated")
+    return out
+
+
+def kvcache_workspace_bytes(B, H, T, frame_len, d, frame_index) -> int:
+    return int(lib().hybrid_attn_kvcache_workspace_bytes(B, H, T, frame_len, d, frame_index))
+
+
+def hybrid_attn_kvcache_forward(q, k, v, k_cache, v_cache, frame_len, frame_index, softmax_scale: float = 0.0,
+                                out=None, workspace=None):
+    """Softmax attention with a full KV cache: k, v ([B, T, H, d]) are written
+    into the caches ([B, cache_frames * frame_len, H, d]) at frame
+    frame_index, then frame n of the call attends to the cache's first
+    (frame_index + n + 1) * frame_len keys."""
+    torch = _torch()
+    if q.device.type != "cuda":
+        raise ValueError("hybrid_attn_kvcache_forward runs on a GPU; tensors must be on a cuda device")
+    B, T, H, d = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    if frame_len <= 0 or T % frame_len:
+        raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
+    cap_t = k_cache.shape[1]
+    if cap_t % frame_len:
+        raise ValueError("the cache length must be a multiple of frame_len")
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(name, t, (B, cap_t, H, d), dt, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, T, H, d), dt, dev)
+    need = kvcache_workspace_bytes(B, H, T, frame_len, d, frame_index)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().hybrid_attn_kvcache_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                           _ptr(workspace), wsb, B, H, T, d, frame_len, cap_t // frame_len,
+                                           frame_index, code, float(softmax_scale), _stream(dev))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_kvcache_forward")
     return out
 
 def hybrid_attn_intra_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame,

@@ -39,6 +39,14 @@
 // units), so exp2 arguments stay <= 8 and accumulator rescales are rare. The
 // result does not depend on that choice: a reference point common to the
 // numerator and the denominator cancels.
+//
+// KV mode (the softmax teacher with a full KV cache that the hybrid layer
+// replaces, ARL2 section 1): the same kernel with frame n's queries attending
+// to the keys [0, kv_off + (n+1) L) of a key/value cache, no readout. The keys
+// of one (b, h, frame) may be split over nsplit work-groups, each writing its
+// unnormalised fp32 output and (max, sum) for a merge pass. Work units
+// (b, h, frame, split) go round-robin over the 8 XCDs, heaviest (latest)
+// frames first, and a unit's query tiles stay on one XCD so they share its L2.
 #include <type_traits>
 
 #include "ha_device.h"
@@ -103,26 +111,43 @@ struct StepFlags {
   static constexpr bool NEXT = NEXT_, TAIL = TAIL_, LOADK = LOADK_;
 };
 
-template <int D>
+template <int D, bool KV>
 __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ qp,
     const float* __restrict__ states, long long stride_bh, long long stride_frame,
     const unsigned char* __restrict__ sfrag, uint16_t* __restrict__ out, int H, int T, int L, int F,
-    int qtiles, int n_items, float c2 /* softmax scale * log2(e) */) {
+    int qtiles, int n_items, float c2 /* softmax scale * log2(e) */,
+    int Tk, int kv_off, int nsplit, float* __restrict__ part_o, float2* __restrict__ part_ml) {
   using C = Cfg<D>;
   constexpr int NCH = C::NCH;
   __shared__ __align__(16) unsigned char smem[C::SMEM];
   unsigned char* const kbuf = smem;                 // two K tiles
   unsigned char* const vbuf = smem + 2 * C::TILE;   // two V tiles
 
-  const int item = xcd_major_item(gridDim.x);
-  if (item >= n_items) return;
-  const int qt = item % qtiles;
-  const int hf = item / qtiles;
-  const int h = hf % H;
-  const int n = (hf / H) % F;
-  const int b = hf / (H * F);
+  int qt, h, n, b, sp = 0;
+  if constexpr (KV) {
+    // unit rank r = (m * 8 + xcd); units ordered latest frame first
+    const int g = blockIdx.x, m = (g >> 3) / qtiles;
+    qt = (g >> 3) % qtiles;
+    const int r = m * 8 + (g & 7);
+    if (r >= n_items) return;
+    sp = r % nsplit;
+    const int r2 = r / nsplit;
+    const int BH = n_items / (F * nsplit);  // n_items = B * H * F * nsplit units
+    const int bh = r2 % BH;
+    n = F - 1 - r2 / BH;
+    b = bh / H;
+    h = bh % H;
+  } else {
+    const int item = xcd_major_item(gridDim.x);
+    if (item >= n_items) return;
+    qt = item % qtiles;
+    const int hf = item / qtiles;
+    h = hf % H;
+    n = (hf / H) % F;
+    b = hf / (H * F);
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,6 +159,24 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   const int span = (int)((uint32_t)(L - 1) * rsb + D * 2);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + fbase), 0, span, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + fbase), 0, span, kRsrcWord3);
+  // KV mode: visible keys [0, nkeys) of the cache, this split's tiles
+  // [t0, t0 + ntiles); each tile gets its own descriptor (32-bit offsets stay
+  // inside one tile however long the cache)
+  int nkeys = L, t0 = 0;
+  long long kvbase = 0;
+  if constexpr (KV) {
+    nkeys = kv_off + (n + 1) * L;
+    const int nt_all = (nkeys + KT - 1) / KT;
+    t0 = (int)((long long)sp * nt_all / nsplit);
+    const int t1 = (int)((long long)(sp + 1) * nt_all / nsplit);
+    kvbase = (long long)b * Tk * ((long long)H * D) + (long long)h * D;
+    nkeys = (t1 == nt_all ? nkeys : t1 * KT) - t0 * KT;  // keys of this split
+  }
+  auto tile_rsrc = [&](const uint16_t* base, int j) {
+    const int rows = nkeys - j * KT < KT ? nkeys - j * KT : KT;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + kvbase + (long long)(t0 + j) * KT * H * D), 0,
+                                             (int)((uint32_t)(rows - 1) * rsb + D * 2), kRsrcWord3);
+  };
 
   const int q0 = qt * QPB + wave * QPW;
   const bool wave_active = q0 < L;
@@ -155,16 +198,18 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     voff0 = row * rsb + ((pc ^ v_swz<NCH>(row)) << 4);
   }
   auto issue_k = [&](int j, int buf) {
-    const uint32_t toff = (uint32_t)j * KT * rsb;
+    const uint32_t toff = KV ? 0u : (uint32_t)j * KT * rsb;
+    const __amdgpu_buffer_rsrc_t r = KV ? tile_rsrc(k, j) : rk;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16_to_lds(rk, kbuf + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
+      dma16_to_lds(r, kbuf + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
   };
   auto issue_v = [&](int j, int buf) {
-    const uint32_t toff = (uint32_t)j * KT * rsb;
+    const uint32_t toff = KV ? 0u : (uint32_t)j * KT * rsb;
+    const __amdgpu_buffer_rsrc_t r = KV ? tile_rsrc(v, j) : rv;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16_to_lds(rv, vbuf + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
+      dma16_to_lds(r, vbuf + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
   };
 
   // ---- per-lane LDS read offsets
@@ -196,8 +241,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l0 = 0.f, l1 = 0.f;
 
-  const int ntiles = (L + KT - 1) / KT;
-  const int last_valid = L - (ntiles - 1) * KT;  // keys in the last tile
+  const int ntiles = (nkeys + KT - 1) / KT;
+  const int last_valid = nkeys - (ntiles - 1) * KT;  // keys in the last tile
 
   // S^T for one tile (two 32-key blocks) from K buffer kb_. MFMA i uses the K
   // operand (ks, kb) = (i/2, i%2); operands are read PF MFMAs ahead.
@@ -371,6 +416,34 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     __syncthreads();
   }
 
+  if constexpr (KV) {  // ---- epilogue without readout
+    const float lsum = sum_across_halves(l0 + l1);
+    if (!wave_active || my_q >= L) return;
+    if (nsplit > 1) {  // unnormalised partial output and (max, sum) of this split
+      const size_t row = (((size_t)sp * (n_items / (H * F * nsplit)) + b) * T + (size_t)n * L + my_q) * H + h;
+      float* po = part_o + row * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+          *reinterpret_cast<f32x4*>(po + db * 32 + 8 * gg + 4 * hh) =
+              f32x4{o[db][4 * gg], o[db][4 * gg + 1], o[db][4 * gg + 2], o[db][4 * gg + 3]};
+      if (hh == 0) part_ml[row] = float2{m_run, lsum};
+      return;
+    }
+    const float inv = 1.f / lsum;
+    uint16_t* op = out + fbase + (long long)my_q * H * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int dv = db * 32 + 8 * gg + 4 * hh;
+        st_global_8B(op + dv, u32x2{pack_bf16x2(o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv),
+                                    pack_bf16x2(o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv)});
+      }
+    }
+    return;
+  } else {
   // ---- epilogue: O = O / l + Q' S_n. S_n reaches LDS either as the bf16
   // readout fragments the state scan wrote (copied as they are), or from the
   // fp32 row-major state, converted here to bf16 [dk][dv].
@@ -453,6 +526,54 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
       }
     }
   }
+  }
+}
+
+// Merge of the key splits: per (b, token, h) row, m = max_s m_s and
+// out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s, splits in order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                         const float2* __restrict__ part_ml,
+                                                         uint16_t* __restrict__ out, long long rows,
+                                                         int nsplit) {
+  constexpr int TPR = D / 8;  // threads per row, 8 outputs each
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / TPR;
+  if (row >= rows) return;
+  const int c0 = (int)(t % TPR) * 8;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[s * rows + row].x);
+  float den = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float2 ml = part_ml[s * rows + row];
+    const float wgt = __builtin_amdgcn_exp2f(ml.x - m);
+    den = fmaf(wgt, ml.y, den);
+    const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * D + c0);
+    const f32x4 a = po[0], b = po[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = fmaf(wgt, a[e], acc[e]);
+      acc[4 + e] = fmaf(wgt, b[e], acc[4 + e]);
+    }
+  }
+  const float inv = 1.f / den;
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + row * D + c0) = r;
+}
+
+// Copy of the call's K, V rows into the cache at token offset `at` of each
+// stream (16 bytes per thread).
+__global__ __launch_bounds__(256) void kv_append_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                                        u32x4* __restrict__ kc, u32x4* __restrict__ vc,
+                                                        long long per_b, long long cap_b, long long at,
+                                                        long long total) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long b = i / per_b, r = i % per_b;
+  kc[b * cap_b + at + r] = k[i];
+  vc[b * cap_b + at + r] = v[i];
 }
 
 }  // namespace
@@ -469,10 +590,59 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                               (const uint16_t*)qp, states, stride_bh, stride_frame,
                               (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
-                              qtiles, (int)items, c2);
+                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr);
   };
-  if (s.d == 128) args(attn_bf16_kernel<128>);
-  else args(attn_bf16_kernel<64>);
+  if (s.d == 128) args(attn_bf16_kernel<128, false>);
+  else args(attn_bf16_kernel<64, false>);
+  return hipGetLastError();
+}
+
+int kv_splits(const Shape& s, int kv_off) {
+  const int qtiles = (s.L + QPB - 1) / QPB;
+  const long long items = (long long)s.B * s.H * s.F * qtiles;
+  if (items >= 256) return 1;
+  const int nt_min = (kv_off + s.L + KT - 1) / KT;  // tiles of the call's first frame
+  int n = (int)((512 + items - 1) / items);
+  if (n > nt_min / 16) n = nt_min / 16;  // at least 16 key tiles per split
+  if (n > 32) n = 32;
+  return n < 1 ? 1 : n;
+}
+
+hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v_cache, void* out, float* part_o,
+                               void* part_ml, int nsplit, int Tk, int kv_off, const Shape& s, float scale,
+                               hipStream_t st) {
+  const int qtiles = (s.L + QPB - 1) / QPB;
+  const int units = s.B * s.H * s.F * nsplit;
+  const int grid = ((units + 7) / 8) * 8 * qtiles;
+  const float c2 = scale * kLog2e;
+  auto args = [&](auto kern) {
+    kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
+                              nullptr, 0, 0, nullptr, (uint16_t*)out, s.H, s.T, s.L, s.F, qtiles, units, c2, Tk,
+                              kv_off, nsplit, part_o, (float2*)part_ml);
+  };
+  if (s.d == 128) args(attn_bf16_kernel<128, true>);
+  else args(attn_bf16_kernel<64, true>);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  const long long rows = (long long)s.B * s.T * s.H;
+  const long long threads = rows * (s.d / 8);
+  if (s.d == 128)
+    attn_merge_kernel<128><<<(int)((threads + 255) / 256), 256, 0, st>>>(part_o, (const float2*)part_ml,
+                                                                         (uint16_t*)out, rows, nsplit);
+  else
+    attn_merge_kernel<64><<<(int)((threads + 255) / 256), 256, 0, st>>>(part_o, (const float2*)part_ml,
+                                                                        (uint16_t*)out, rows, nsplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const void* k, const void* v, void* k_cache, void* v_cache, int cache_tokens,
+                            int at_token, const Shape& s, hipStream_t st) {
+  const long long per_b = (long long)s.T * s.H * s.d * 2 / 16;  // 16-byte pieces per stream
+  const long long cap_b = (long long)cache_tokens * s.H * s.d * 2 / 16;
+  const long long at = (long long)at_token * s.H * s.d * 2 / 16;
+  const long long total = per_b * s.B;
+  kv_append_kernel<<<(int)((total + 255) / 256), 256, 0, st>>>((const u32x4*)k, (const u32x4*)v, (u32x4*)k_cache,
+                                                              (u32x4*)v_cache, per_b, cap_b, at, total);
   return hipGetLastError();
 }
 

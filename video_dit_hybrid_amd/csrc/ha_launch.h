@@ -21,6 +21,21 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
                             const void* sfrag, void* out, const Shape& s, float scale,
                             hipStream_t st);
 
+// KV mode of the same kernel (the softmax teacher with a full KV cache): the
+// queries of call frame n (q, out [B, T, H, d], T = F * L) attend to the keys
+// [0, kv_off + (n+1) L) of k_cache, v_cache [B, Tk, H, d]; no readout. With
+// nsplit > 1 the keys of each (b, h, frame) are split over nsplit work-groups
+// whose partial outputs (part_o: nsplit * B * T * H * d fp32, part_ml:
+// nsplit * B * T * H float2) a merge pass adds up. kv_splits gives the split
+// count (shape only: equal shapes give bitwise equal results).
+int kv_splits(const Shape& s, int kv_off);
+hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v_cache, void* out, float* part_o,
+                               void* part_ml, int nsplit, int Tk, int kv_off, const Shape& s, float scale,
+                               hipStream_t st);
+// k, v [B, T, H, d] bf16 -> the cache [B, cache_tokens, H, d] at token at_token.
+hipError_t launch_kv_append(const void* k, const void* v, void* k_cache, void* v_cache, int cache_tokens,
+                            int at_token, const Shape& s, hipStream_t st);
+
 // The same on fp32 operands (fp32 FMA).
 hipError_t launch_attn_fp32(const void* q, const void* k, const void* v, const void* qp,
                             const float* states, long long stride_bh, long long stride_frame,

@@ -414,3 +414,68 @@ ha_status hybrid_attn_gates(const void* x, const void* w_gate, const float* b_ga
 }
 
 }  // extern "C"
+
+// ---- the softmax teacher with a full KV cache (attn_bf16.hip, KV mode): the
+// call's K, V rows are appended to the cache at frame frame_index, then frame
+// n of the call attends to the cache's first (frame_index + n + 1) * L keys.
+namespace {
+struct KvWs {
+  size_t part_o, part_ml, total;
+  int nsplit;
+};
+KvWs kv_layout(const ha::Shape& s, int frame_index) {
+  KvWs w{0, 0, 0, 1};
+  w.nsplit = ha::kv_splits(s, frame_index * s.L);
+  if (w.nsplit == 1) return w;
+  const size_t rows = (size_t)s.B * s.T * s.H;
+  w.part_o = 0;
+  w.part_ml = align_up((size_t)w.nsplit * rows * s.d * 4);
+  w.total = w.part_ml + align_up((size_t)w.nsplit * rows * 8);
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+size_t hybrid_attn_kvcache_workspace_bytes(int B, int H, int T, int frame_len, int d, int frame_index) {
+  ha::Shape s;
+  if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK || frame_index < 0) return 0;
+  return kv_layout(s, frame_index).total;
+}
+
+ha_status hybrid_attn_kvcache_forward(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                                      void* out, void* workspace, size_t workspace_bytes, int B, int H, int T,
+                                      int d, int frame_len, int cache_frames, int frame_index, ha_dtype dtype,
+                                      float softmax_scale, void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (dtype != HA_BF16) return HA_ERR_UNSUPPORTED;
+  if (frame_index < 0 || cache_frames <= 0 || (long long)frame_index + s.F > cache_frames) return HA_ERR_SHAPE;
+  if ((long long)cache_frames * frame_len > kMaxItems) return HA_ERR_SHAPE;
+  if (!q || !k || !v || !k_cache || !v_cache || !out) return HA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 16) || (workspace && !aligned(workspace, 16)))
+    return HA_ERR_ALIGN;
+  const KvWs lay = kv_layout(s, frame_index);
+  if (lay.total && (!workspace || workspace_bytes < lay.total)) return HA_ERR_WORKSPACE;
+  const size_t tb = tensor_bytes(s, dtype);
+  const size_t cb = (size_t)B * cache_frames * frame_len * H * (size_t)d * 2;
+  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
+      overlap(out, tb, k_cache, cb) || overlap(out, tb, v_cache, cb) || overlap(out, tb, workspace, lay.total) ||
+      overlap(k_cache, cb, v_cache, cb) || overlap(k, tb, k_cache, cb) || overlap(v, tb, k_cache, cb) ||
+      overlap(k, tb, v_cache, cb) || overlap(v, tb, v_cache, cb) || overlap(q, tb, k_cache, cb) ||
+      overlap(q, tb, v_cache, cb) || overlap(workspace, lay.total, k_cache, cb) ||
+      overlap(workspace, lay.total, v_cache, cb))
+    return HA_ERR_ALIAS;
+  hipStream_t st = (hipStream_t)stream;
+  const int cap = cache_frames * frame_len;
+  if (ha::launch_kv_append(k, v, k_cache, v_cache, cap, frame_index * frame_len, s, st) != hipSuccess)
+    return HA_ERR_DEVICE;
+  char* ws = (char*)workspace;
+  return launched(ha::launch_attn_kv_bf16(q, k_cache, v_cache, out, lay.total ? (float*)(ws + lay.part_o) : nullptr,
+                                          lay.total ? (void*)(ws + lay.part_ml) : nullptr, lay.nsplit, cap,
+                                          frame_index * frame_len, s, resolve_scale(softmax_scale, d), st));
+}
+
+}  // extern "C"
