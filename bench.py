@@ -7,6 +7,9 @@ applied inside the call) and --variant gated (gates projected from the layer
 input x, maps, L2-normalised K'), each against the same prologue done by
 separate torch ops before hybrid_attn_forward.
 
+--baseline kvcache: the softmax teacher with a full KV cache against the
+hybrid layer, per streamed frame as the video grows (81 to 921 frames).
+
 Other workloads (not the headline line): --workload 720p (one clean call,
 H=40, 21 x 3600 tokens); --workload stream (120 frames, each 4 query-only
 denoise calls + 1 clean call, F=1 per call; frames/s over all 600 calls);
@@ -326,6 +329,96 @@ def bench_variant(w, args):
                                  "bytes_per_launch": gbytes, "avg_launch_ms": round(gms, 4)}
     print(json.dumps(res), flush=True)
 
+
+def bench_kvcache(args):
+    """Per-layer cost of one streamed frame (4 denoising passes + 1 clean pass,
+    one frame per call, 480p shape B1 H12 d128 L1560) for the softmax teacher
+    with a full KV cache (hybrid_attn_kvcache_forward: frame n attends to n+1
+    frames of keys) and for the hybrid layer (hybrid_attn_forward: constant
+    work per frame), at sampled frame indices up to --kv-frames latent frames;
+    whole-video times by linear interpolation of the per-frame cost; KV-cache
+    and state bytes of one layer."""
+    import torch
+    from video_dit_hybrid_amd import api
+    from video_dit_hybrid_amd import workloads as W
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS["stream"]
+    B, H, d, L, P = w.B, w.H, w.d, w.L, w.denoise_passes + 1
+    nmax = args.kv_frames
+    log(f"bench: kv-cache teacher vs hybrid, up to {nmax} latent frames")
+    passes = []
+    for p in range(P):
+        inp = W.make_call_inputs(w, 0, 1, p, clean=(p == P - 1))
+        passes.append({k: W.as_torch(v, "bf16" if k in W.QKV_NAMES else "fp32", dev) for k, v in inp.items()})
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    kc = torch.randn((B, nmax * L, H, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vc = torch.randn((B, nmax * L, H, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = torch.empty_like(passes[0]["q"])
+    ws = torch.empty(max(1, api.kvcache_workspace_bytes(B, H, L, L, d, nmax - 1)), dtype=torch.uint8, device=dev)
+    state = torch.from_numpy(W.make_state0(w)).to(dev)
+    hws = torch.empty(max(1, api.workspace_bytes(B, H, L, L, d, 1)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def kv_frame(n):
+        for t in passes:
+            api.hybrid_attn_kvcache_forward(t["q"], t["k"], t["v"], kc, vc, L, n, out=out, workspace=ws)
+
+    def hyb_frame():
+        for p, t in enumerate(passes):
+            if p < P - 1:
+                api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], None, None, None, None, state, L, 0,
+                                        out=out, workspace=hws)
+            else:
+                api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], t["kp"], t["vp"], t["alpha"], t["beta"],
+                                        state, L, 1, out=out, workspace=hws)
+
+    def ev_time(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_h = ev_time(hyb_frame, 20)
+    samples = sorted({n for n in (0, 10, 20, 40, 80, 120, 160, 200, nmax - 1) if n < nmax})
+    t_kv = {}
+    for n in samples:
+        t_kv[n] = ev_time(lambda: kv_frame(n), 3 if n > 40 else 10)
+        log(f"bench: frame {n}: kv {t_kv[n]:.3f} ms, hybrid {t_h:.3f} ms")
+
+    def kv_at(n):  # linear interpolation of the per-frame cost (it is affine in n)
+        lo = max(x for x in samples if x <= n)
+        hi = min(x for x in samples if x >= n)
+        return t_kv[lo] if hi == lo else t_kv[lo] + (t_kv[hi] - t_kv[lo]) * (n - lo) / (hi - lo)
+
+    curve = []
+    for lat in (21, 41, 81, 161, 231):
+        if lat > nmax:
+            continue
+        kv_total = sum(kv_at(n) for n in range(lat))
+        curve.append({"video_frames": 4 * (lat - 1) + 1, "latent_frames": lat,
+                      "kv_cache_ms": round(kv_total, 2), "hybrid_ms": round(lat * t_h, 2),
+                      "speedup": round(kv_total / (lat * t_h), 2),
+                      "kv_cache_bytes": 2 * lat * L * H * d * 2 * B, "hybrid_state_bytes": B * H * d * d * 4})
+    n_last = samples[-1]
+    flop_last = P * 4.0 * L * (n_last + 1) * L * d * H * B
+    res = {"metric": "per-layer time of one streamed frame (4 denoise + 1 clean pass): KV-cache softmax teacher vs "
+                     f"hybrid layer, 480p shape, frame {n_last}, 1 MI355X",
+           "value": round(t_kv[n_last] / t_h, 2), "unit": "x (teacher time / hybrid time)", "n_gpus": 1,
+           "higher_is_better": True, "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "480p streaming, one frame per call", "B": B, "H": H, "d": d, "frame_len": L,
+                      "passes_per_frame": P},
+           "hybrid_ms_per_frame": round(t_h, 4),
+           "kv_cache_ms_per_frame": {str(n): round(t, 4) for n, t in t_kv.items()},
+           "kv_attention_tflops_at_last": round(flop_last / (t_kv[n_last] / 1e3) / 1e12, 1),
+           "video_curve": curve}
+    print(json.dumps(res), flush=True)
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +430,10 @@ def main():
     ap.add_argument("--variant", choices=["plain", "fmap", "gated"], default="plain",
                     help="plain: the layer on given Q', K', V', alpha, beta (the headline); fmap / gated: the "
                          "prologue (maps; gates from x) inside the call, against an unfused torch prologue")
+    ap.add_argument("--baseline", choices=["kvcache"], default=None,
+                    help="kvcache: per-frame cost of the KV-cache softmax teacher against the hybrid layer "
+                         "as the video grows")
+    ap.add_argument("--kv-frames", type=int, default=231, help="latent frames of the longest video (231 = 921 frames)")
     ap.add_argument("--kernel", choices=["attn", "update", "copy"], default=None,
                     help="launch only one phase (readout-only attention, or the state update) "
                          "steps times, for profilers; prints its average time")
@@ -351,6 +448,9 @@ def main():
     from video_dit_hybrid_amd import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.baseline == "kvcache":
+        bench_kvcache(args)
+        return
     if args.variant != "plain":
         if w.frames_per_call or w.dtype != "bf16":
             print("--variant runs one bf16 clean call over a whole workload (480p, 720p)", file=sys.stderr)
