@@ -561,7 +561,7 @@ def main():
     traffic = traffic_for_current_kernel() if w.name == "480p" else None
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "kernel": "attn_bf16_kernel<128> (intra-frame softmax + Q'S readout)",
+            "kernel": "attn_bf16_kernel<128, false> (intra-frame softmax + Q'S readout)",
             "flop_per_launch": att + rd, "avg_launch_ms": round(attn_ms, 4)}
     # The core clock under this kernel is well below the 2.4 GHz the peak
     # assumes. Its core-clock cycles per launch (rocprofv3 GRBM_GUI_ACTIVE, a
