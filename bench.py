@@ -9,6 +9,8 @@ separate torch ops before hybrid_attn_forward.
 
 --baseline kvcache: the softmax teacher with a full KV cache against the
 hybrid layer, per streamed frame as the video grows (81 to 921 frames).
+--stack: a 30-layer attention stack with 0, 50, 75 and 100 % hybrid layers
+(the rest softmax with KV caches), per frame and per video, with memory.
 
 Other workloads (not the headline line): --workload 720p (one clean call,
 H=40, 21 x 3600 tokens); --workload stream (120 frames, each 4 query-only
@@ -419,6 +421,82 @@ def bench_kvcache(args):
            "video_curve": curve}
     print(json.dumps(res), flush=True)
 
+
+def bench_stack(args):
+    """The 30-layer attention stack of a streaming 480p model (B1 H12 d128,
+    1560-token frames, 4 denoising + 1 clean pass per frame) with 0 %, 50 %,
+    75 % and 100 % of its layers hybrid and the rest softmax with a full KV
+    cache: time of one frame through all layers at sampled frame indices,
+    whole-video times by interpolation (the per-frame cost is affine in the
+    frame index), and the bytes of caches and states. Each configuration
+    allocates its caches for --kv-frames frames up front."""
+    import torch
+    from video_dit_hybrid_amd import workloads as W
+    from video_dit_hybrid_amd.stack import AttentionStack, layer_kinds
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS["stream"]
+    B, H, d, L, P = w.B, w.H, w.d, w.L, w.denoise_passes + 1
+    nmax, n_layers = args.kv_frames, 30
+    passes = []
+    for p in range(P):
+        inp = W.make_call_inputs(w, 0, 1, p, clean=(p == P - 1))
+        passes.append({k: W.as_torch(v, "bf16" if k in W.QKV_NAMES else "fp32", dev) for k, v in inp.items()})
+    out = torch.empty_like(passes[0]["q"])
+    stream = torch.cuda.current_stream(dev)
+    samples = sorted({n for n in (0, 20, 80, 160, nmax - 1) if n < nmax})
+    rows = []
+    for frac in (0.0, 0.5, 0.75, 1.0):
+        kinds = layer_kinds(n_layers, frac)
+        stack = AttentionStack(kinds, B, H, d, L, nmax, dev)
+        for kind, c in zip(stack.kinds, stack.caches):  # caches hold values (any), not garbage
+            if c is not None:
+                c[0].normal_()
+                c[1].normal_()
+        t = {}
+        for n in samples:
+            stack.run_frame(n, passes, out)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 2
+            e0.record(stream)
+            for _ in range(reps):
+                stack.run_frame(n, passes, out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t[n] = e0.elapsed_time(e1) / reps
+            log(f"bench: stack {kinds.count('hybrid')}/{n_layers} hybrid, frame {n}: {t[n]:.2f} ms")
+
+        def at(n):
+            lo = max(x for x in samples if x <= n)
+            hi = min(x for x in samples if x >= n)
+            return t[lo] if hi == lo else t[lo] + (t[hi] - t[lo]) * (n - lo) / (hi - lo)
+
+        videos = {}
+        for lat in (21, 81, 161, 231):
+            if lat <= nmax:
+                videos[str(4 * (lat - 1) + 1)] = {"ms": round(sum(at(n) for n in range(lat)), 1),
+                                                 "cache_gb": round(stack.cache_bytes(lat) / 1e9, 3),
+                                                 "state_gb": round(stack.state_bytes() / 1e9, 6)}
+        rows.append({"hybrid_layers": kinds.count("hybrid"), "ms_per_frame": {str(n): round(v, 3) for n, v in t.items()},
+                     "videos": videos})
+        del stack
+        torch.cuda.empty_cache()
+    base = rows[0]["videos"]
+    for r in rows:
+        for k, v in r["videos"].items():
+            v["speedup_vs_softmax"] = round(base[k]["ms"] / v["ms"], 2)
+            v["memory_saving"] = round(1 - (v["cache_gb"] + v["state_gb"]) / (base[k]["cache_gb"] + base[k]["state_gb"]), 3)
+    longest = str(4 * (max(x for x in (21, 81, 161, 231) if x <= nmax) - 1) + 1)
+    half = next(r for r in rows if r["hybrid_layers"] == 15)
+    res = {"metric": f"attention-stack time of a {longest}-frame 480p video, 30 layers with 15 hybrid, speed-up over "
+                     "all-softmax with KV caches, 1 MI355X",
+           "value": half["videos"][longest]["speedup_vs_softmax"], "unit": "x", "n_gpus": 1,
+           "higher_is_better": True, "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "480p streaming attention stack, 30 layers, one frame per call", "B": B, "H": H,
+                      "d": d, "frame_len": L, "passes_per_frame": P, "layer_choice": "hybrid layers spread evenly"},
+           "configs": rows}
+    print(json.dumps(res), flush=True)
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -433,6 +511,8 @@ def main():
     ap.add_argument("--baseline", choices=["kvcache"], default=None,
                     help="kvcache: per-frame cost of the KV-cache softmax teacher against the hybrid layer "
                          "as the video grows")
+    ap.add_argument("--stack", action="store_true",
+                    help="the 30-layer attention stack with 0/50/75/100 %% hybrid layers, streamed frames")
     ap.add_argument("--kv-frames", type=int, default=231, help="latent frames of the longest video (231 = 921 frames)")
     ap.add_argument("--kernel", choices=["attn", "update", "copy"], default=None,
                     help="launch only one phase (readout-only attention, or the state update) "
@@ -450,6 +530,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.baseline == "kvcache":
         bench_kvcache(args)
+        return
+    if args.stack:
+        bench_stack(args)
         return
     if args.variant != "plain":
         if w.frames_per_call or w.dtype != "bf16":
