@@ -46,6 +46,12 @@ section 4: the baselines' memory and time grow with video length) is here too
 (chunk_causal_attention): the queries of frame N attend to the keys of frames
 0..N, bidirectionally inside frame N.
 
+The token-level access variant (ARL2 section 4 ablations: token-level
+instead of frame-level access degrades quality; it is the canonical,
+per-token gated delta rule) is here as hybrid_layer_token_level: every token
+reads the state left by all earlier tokens, and every token of a clean pass
+writes it; the frame's forget gate applies once, at its first token.
+
 Every function here is pinned by tests/test_oracle_pins.py against
 properties the page and the mathematics fix (row sums, closed forms, the
 delta-rule recall property, brute force on tiny inputs, textbook attention).
@@ -258,3 +264,31 @@ def chunk_causal_attention(q, k, v, frame_len, scale=None):
         vis = slice(0, (n + 1) * L)
         out[r] = intra_frame_attention(q[r], k[vis], v[vis], scale)
     return out
+
+
+def hybrid_layer_token_level(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale=None):
+    """The layer with token-level access (the ablated alternative to ARL2
+    2.2's frame-level access), one (stream, head): tokens in order, token t of
+    frame N reads S_{t-1}, the state after every earlier token, then
+        S_t = a_t S_{t-1} + beta_t k'_t^T (v'_t - k'_t S_{t-1}),
+    a_t = alpha_N for the first token of frame N and 1 for the others (the
+    frame's decay applied once, the residual against the undecayed state as in
+    the frame-level rule). out = intra-frame softmax (unchanged) + q'_t S_{t-1}.
+    With update_state = 0 the per-token states are still what the tokens read
+    (the pass's own tokens update a transient copy) and the input state is
+    returned unchanged.
+
+    q..vp: [T, d]; alpha: [F]; beta: [T]; state: [d, d]. Returns (out, state).
+    """
+    T, d = q.shape
+    L = int(frame_len)
+    S = np.array(state, dtype=np.float64, copy=True)
+    out = np.empty((T, vp.shape[1]), dtype=np.float64)
+    for n in range(T // L):
+        r = slice(n * L, (n + 1) * L)
+        out[r] = intra_frame_attention(q[r], k[r], v[r], scale)
+    for t in range(T):
+        out[t] += qp[t] @ S
+        a = float(alpha[t // L]) if t % L == 0 else 1.0
+        S = a * S + float(beta[t]) * np.outer(kp[t], vp[t] - kp[t] @ S)
+    return out, (S if update_state else np.array(state, dtype=np.float64, copy=True))

@@ -594,7 +594,110 @@ def check_chunk_causal_causality_and_streaming(o):
     assert np.allclose(last, out[12:], rtol=1e-13, atol=1e-14)
 
 
+
+# --- token-level access ----------------------------------------------------------
+
+def _tok_inputs(rng, T=12, d=4, L=4):
+    q, k, v, qp, kp, vp = (rng.standard_normal((T, d)) for _ in range(6))
+    kp = kp / np.linalg.norm(kp, axis=1, keepdims=True)
+    a = rng.uniform(0.5, 0.95, T // L)
+    b = rng.uniform(0.05, 0.4, T)
+    S0 = 0.3 * rng.standard_normal((d, d))
+    return q, k, v, qp, kp, vp, a, b, S0
+
+
+def check_token_level_one_token_frames(o):
+    """L = 1: every frame is one token, so token-level and frame-level access
+    coincide; the same layer through hybrid_layer_head."""
+    rng = np.random.default_rng(51)
+    q, k, v, qp, kp, vp, a, b, S0 = _tok_inputs(rng, T=6, L=1)
+    out, S = o.hybrid_layer_token_level(q, k, v, qp, kp, vp, a, b, S0, 1, 1)
+    out2, S2 = o.hybrid_layer_head(q, k, v, qp, kp, vp, a, b, S0, 1, 1)
+    assert np.allclose(out, out2, rtol=1e-13, atol=1e-14) and np.allclose(S, S2, rtol=1e-13, atol=1e-14)
+
+
+def check_token_level_beta0_closed_form(o):
+    """beta = 0: the first token of frame N reads (prod_{m<N} alpha_m) S_0, the
+    others (prod_{m<=N} alpha_m) S_0; the final state is (prod alpha) S_0."""
+    rng = np.random.default_rng(52)
+    q, k, v, qp, kp, vp, a, b, S0 = _tok_inputs(rng)
+    out, S = o.hybrid_layer_token_level(q, k, v, qp, kp, vp, a, 0 * b, S0, 4, 1)
+    intra = np.concatenate([o.intra_frame_attention(q[i:i + 4], k[i:i + 4], v[i:i + 4]) for i in (0, 4, 8)])
+    for t in range(12):
+        n = t // 4
+        f = np.prod(a[:n]) * (1.0 if t % 4 == 0 else a[n])
+        assert np.allclose(out[t] - intra[t], f * (qp[t] @ S0), rtol=1e-12, atol=1e-13)
+    assert np.allclose(S, np.prod(a) * S0, rtol=1e-13, atol=1e-15)
+
+
+def check_token_level_brute_force_and_recall(o):
+    """Scalar loops over tokens; with beta = 1, alpha = 1 and unit keys each
+    token's write is recalled exactly: k'_t S_t = v'_t (the delta rule)."""
+    rng = np.random.default_rng(53)
+    q, k, v, qp, kp, vp, a, b, S0 = _tok_inputs(rng, T=6, d=3, L=3)
+    out, S = o.hybrid_layer_token_level(q, k, v, qp, kp, vp, a, b, S0, 3, 1)
+    d = 3
+    St = [[S0[i][j] for j in range(d)] for i in range(d)]
+    for t in range(6):
+        inter = [sum(qp[t][i] * St[i][j] for i in range(d)) for j in range(d)]
+        n = t // 3
+        want = o.intra_frame_attention(q[n * 3:(n + 1) * 3], k[n * 3:(n + 1) * 3], v[n * 3:(n + 1) * 3])[t % 3]
+        for j in range(d):
+            assert abs(out[t][j] - (want[j] + inter[j])) < 1e-12
+        aa = a[n] if t % 3 == 0 else 1.0
+        ks = [sum(kp[t][i] * St[i][j] for i in range(d)) for j in range(d)]
+        St = [[aa * St[i][j] + b[t] * kp[t][i] * (vp[t][j] - ks[j]) for j in range(d)] for i in range(d)]
+    assert np.allclose(S, np.array(St), rtol=1e-12, atol=1e-13)
+    # recall
+    _, S1 = o.hybrid_layer_token_level(q[:1], k[:1], v[:1], qp[:1], kp[:1], vp[:1], np.ones(1), np.ones(1), S0, 1, 1)
+    assert np.allclose(kp[0] @ S1, vp[0], rtol=1e-12, atol=1e-12)
+
+
+def check_token_level_chunked_wy_form(o):
+    """The chunked form the GPU path evaluates (exact algebra): for a chunk of
+    tokens inside one frame with entry state S and decay a (alpha of the frame
+    for its first chunk, else 1), D = diag(1, a, .., a), T = (I + strict_lower(
+    diag(beta) K K^T))^-1, X = T diag(beta) V - T diag(beta) D K S; then
+    S_end = a S + K^T X and the tokens read c_t S + sum_{j<t} (q_t.k_j) X_j,
+    c = (1, a, .., a). Chunks of 3 tokens over frames of 6."""
+    rng = np.random.default_rng(54)
+    q, k, v, qp, kp, vp, a, b, S0 = _tok_inputs(rng, T=12, d=4, L=6)
+    out, Sf = o.hybrid_layer_token_level(q, k, v, qp, kp, vp, a, b, S0, 6, 1)
+    intra = np.concatenate([o.intra_frame_attention(q[i:i + 6], k[i:i + 6], v[i:i + 6]) for i in (0, 6)])
+    S = S0.copy()
+    for c0 in range(0, 12, 3):
+        r = slice(c0, c0 + 3)
+        dec = a[c0 // 6] if c0 % 6 == 0 else 1.0
+        K, V, Q, bt = kp[r], vp[r], qp[r], b[r]
+        Dv = np.array([1.0, dec, dec])
+        Tm = np.linalg.inv(np.eye(3) + np.tril(bt[:, None] * (K @ K.T), -1))
+        X = Tm @ (bt[:, None] * V) - Tm @ ((bt * Dv)[:, None] * K) @ S
+        inter = Dv[:, None] * (Q @ S) + np.tril(Q @ K.T, -1) @ X
+        assert np.allclose(out[r] - intra[r], inter, rtol=1e-11, atol=1e-12)
+        S = dec * S + K.T @ X
+    assert np.allclose(S, Sf, rtol=1e-11, atol=1e-12)
+
+
+def check_token_level_denoise_and_causality(o):
+    """update_state = 0 returns the input state and the same outputs; perturbing
+    token j moves the inter-frame outputs of later tokens only."""
+    rng = np.random.default_rng(55)
+    q, k, v, qp, kp, vp, a, b, S0 = _tok_inputs(rng)
+    out, S = o.hybrid_layer_token_level(q, k, v, qp, kp, vp, a, b, S0, 4, 1)
+    out0, S_0 = o.hybrid_layer_token_level(q, k, v, qp, kp, vp, a, b, S0, 4, 0)
+    assert np.array_equal(out0, out) and np.array_equal(S_0, S0)
+    vp2 = vp.copy()
+    vp2[5] += 1.0
+    out2, _ = o.hybrid_layer_token_level(q, k, v, qp, kp, vp2, a, b, S0, 4, 1)
+    assert np.array_equal(out2[:6], out[:6]) and not np.allclose(out2[6], out[6])
+
+
 ALL_CHECKS = [
+    check_token_level_one_token_frames,
+    check_token_level_beta0_closed_form,
+    check_token_level_brute_force_and_recall,
+    check_token_level_chunked_wy_form,
+    check_token_level_denoise_and_causality,
     check_chunk_causal_single_frame,
     check_chunk_causal_is_block_masked_sdpa,
     check_chunk_causal_brute_force,

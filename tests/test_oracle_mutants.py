@@ -211,7 +211,29 @@ def _causal_variant(m, lo=None, hi=None, token_causal=False):
     m.chunk_causal_attention = f
 
 
+
+def _token_variant(m, decay_every_token=False, read_after=False, decayed_residual=False):
+    def f(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, scale=None):
+        T, L = q.shape[0], int(frame_len)
+        S = np.array(state, dtype=np.float64, copy=True)
+        out = np.empty_like(vp, dtype=np.float64)
+        for n in range(T // L):
+            r = slice(n * L, (n + 1) * L)
+            out[r] = m.intra_frame_attention(q[r], k[r], v[r], scale)
+        for t in range(T):
+            a = float(alpha[t // L]) if (t % L == 0 or decay_every_token) else 1.0
+            base = a * S if decayed_residual else S
+            Sn = a * S + float(beta[t]) * np.outer(kp[t], vp[t] - kp[t] @ base)
+            out[t] += qp[t] @ (Sn if read_after else S)
+            S = Sn
+        return out, (S if update_state else np.array(state, dtype=np.float64, copy=True))
+    m.hybrid_layer_token_level = f
+
+
 MUTANTS = {
+    "token_decay_every_token": lambda m: _token_variant(m, decay_every_token=True),
+    "token_reads_own_write": lambda m: _token_variant(m, read_after=True),
+    "token_decayed_residual": lambda m: _token_variant(m, decayed_residual=True),
     "causal_sees_next_frame": lambda m: _causal_variant(m, hi=lambda n, L: (n + 2) * L),
     "causal_misses_own_frame": lambda m: _causal_variant(m, hi=lambda n, L: max(n, 1) * L),
     "causal_own_frame_only": lambda m: _causal_variant(m, lo=lambda n, L: n * L),
