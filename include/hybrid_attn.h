@@ -270,6 +270,37 @@ ha_status hybrid_attn_kvcache_forward(const void* q, const void* k, const void* 
                                       int cache_frames, int frame_index, ha_dtype dtype,
                                       float softmax_scale, void* stream);
 
+/*
+ * Bytes of workspace hybrid_attn_forward_token_level needs: 96 KiB of
+ * operands per 64-token chunk (B * H * F * ceil(frame_len / 64) chunks) and
+ * the fp32 inter-frame output (B * T * H * d floats), 256-byte aligned.
+ * Returns 0 for invalid sizes or d != 128.
+ */
+size_t hybrid_attn_token_level_workspace_bytes(int B, int H, int T, int frame_len, int d);
+
+/*
+ * The layer with token-level instead of frame-level access (the alternative
+ * the ARL2 ablations compare against, section 4; the canonical per-token
+ * gated delta rule): tokens in order, token t of frame N reads S_{t-1}, the
+ * state after every earlier token, and then writes
+ *   S_t = a_t S_{t-1} + beta_t k'_t^T (v'_t - k'_t S_{t-1}),
+ * a_t = alpha_N for the frame's first token and 1 for the others;
+ * out = intra-frame softmax (as hybrid_attn_forward) + q'_t S_{t-1}.
+ * Arguments and layouts as hybrid_attn_forward. With update_state 0 the
+ * tokens still read the states their predecessors in the call leave (a
+ * transient copy) and `state` is left unchanged; kp, vp, alpha and beta are
+ * required either way. bf16 and d = 128 only (HA_ERR_UNSUPPORTED otherwise);
+ * the workspace is required.
+ */
+ha_status hybrid_attn_forward_token_level(const void* q, const void* k, const void* v,
+                                          const void* qp, const void* kp, const void* vp,
+                                          const float* alpha, const float* beta,
+                                          float* state, void* out,
+                                          void* workspace, size_t workspace_bytes,
+                                          int B, int H, int T, int d, int frame_len,
+                                          ha_dtype dtype, int update_state,
+                                          float softmax_scale, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* hybrid_attn_status_string(int status);
 

@@ -205,3 +205,22 @@ def test_kvcache_workspace_and_validation():
     # a long cache with one frame of queries needs split workspace
     assert kv(T=1560, L=1560, H=12, d=128, cap=40, fi=30, q=1 << 33, k=1 << 34, v=1 << 35, kc=1 << 36,
               vc=1 << 37, out=1 << 38) == 5
+
+
+def test_token_level_workspace_and_validation():
+    up = lambda x: (x + 255) // 256 * 256
+    L, H, d, F = 1560, 12, 128, 21
+    chunks = H * F * 25
+    assert api.token_level_workspace_bytes(1, H, F * L, L, d) == up(chunks * 96 * 1024) + up(F * L * H * d * 4)
+    assert api.token_level_workspace_bytes(1, H, F * L, L, 64) == 0
+
+    def tl(d=128, dtype=0, q=4096, kp=8192, ws=1 << 40, wsb=1 << 40, out=1 << 41):
+        p = lambda x: None if x is None else P(x)
+        return api.lib().hybrid_attn_forward_token_level(p(q), P(12288), P(16384), P(20480), p(kp), P(24576),
+                                                         P(28672), P(32768), P(36864), p(out), p(ws), wsb, 1, 2, 64,
+                                                         d, 32, dtype, 1, 0.0, None)
+    assert tl(d=64) == 3 and tl(dtype=1) == 3
+    assert tl(kp=None) == 1 and tl(ws=None) == 1
+    assert tl(q=4100) == 4
+    assert tl(wsb=64) == 5
+    assert tl(out=8192) == 7

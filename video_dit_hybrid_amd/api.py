@@ -18,7 +18,8 @@ EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_in
            "hybrid_attn_status_string", "hybrid_attn_version", "hybrid_attn_forward_fmap",
            "hybrid_attn_fmap_workspace_bytes", "hybrid_attn_forward_gated",
            "hybrid_attn_gated_workspace_bytes", "hybrid_attn_gates", "hybrid_attn_gates_workspace_bytes",
-           "hybrid_attn_kvcache_forward", "hybrid_attn_kvcache_workspace_bytes")
+           "hybrid_attn_kvcache_forward", "hybrid_attn_kvcache_workspace_bytes",
+           "hybrid_attn_forward_token_level", "hybrid_attn_token_level_workspace_bytes")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_attn.so")
 _lib = None
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.hybrid_attn_kvcache_forward.restype = i
     L.hybrid_attn_kvcache_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.hybrid_attn_kvcache_workspace_bytes.restype = sz
+    L.hybrid_attn_forward_token_level.argtypes = [vp] * 11 + [sz, i, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_forward_token_level.restype = i
+    L.hybrid_attn_token_level_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.hybrid_attn_token_level_workspace_bytes.restype = sz
     L.hybrid_attn_status_string.argtypes = [i]
     L.hybrid_attn_status_string.restype = ctypes.c_char_p
     L.hybrid_attn_version.argtypes = []
@@ -330,6 +335,45 @@ def hybrid_attn_kvcache_forward(q, k, v, k_cache, v_cache, frame_len, frame_inde
                                            frame_index, code, float(softmax_scale), _stream(dev))
     if st != 0:
         raise HybridAttnError(st, "hybrid_attn_kvcache_forward")
+    return out
+
+
+def token_level_workspace_bytes(B, H, T, frame_len, d) -> int:
+    return int(lib().hybrid_attn_token_level_workspace_bytes(B, H, T, frame_len, d))
+
+
+def hybrid_attn_forward_token_level(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state,
+                                    softmax_scale: float = 0.0, out=None, workspace=None):
+    """The layer with token-level access (per-token gated delta rule; the
+    alternative to frame-level access), same arguments as hybrid_attn_forward;
+    kp, vp, alpha, beta are required also when update_state is 0."""
+    torch = _torch()
+    if q.device.type != "cuda":
+        raise ValueError("hybrid_attn_forward_token_level runs on a GPU; tensors must be on a cuda device")
+    B, T, H, d = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    F = T // frame_len if frame_len > 0 and T % frame_len == 0 else -1
+    if F <= 0:
+        raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
+    for name, t in (("k", k), ("v", v), ("qp", qp), ("kp", kp), ("vp", vp)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    _check("alpha", alpha, (B, F, H), torch.float32, dev)
+    _check("beta", beta, (B, T, H), torch.float32, dev)
+    _check("state", state, (B, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, T, H, d), dt, dev)
+    need = token_level_workspace_bytes(B, H, T, frame_len, d)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().hybrid_attn_forward_token_level(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, T, d, frame_len, code,
+        int(bool(update_state)), float(softmax_scale), _stream(dev))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_forward_token_level")
     return out
 
 def hybrid_attn_intra_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame,

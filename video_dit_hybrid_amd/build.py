@@ -22,7 +22,7 @@ LIB_NAME = "libhybrid_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["hybrid_attn.hip", "attn_bf16.hip", "state_bf16.hip", "state_scan.hip", "fp32_path.hip", "fmap.hip",
-           "gates.hip"]
+           "gates.hip", "token_level.hip"]
 ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     const float* __restrict__ states, long long stride_bh, long long stride_frame,
     const unsigned char* __restrict__ sfrag, uint16_t* __restrict__ out, int H, int T, int L, int F,
     int qtiles, int n_items, float c2 /* softmax scale * log2(e) */,
-    int Tk, int kv_off, int nsplit, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    int Tk, int kv_off, int nsplit, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    const float* __restrict__ add_o) {
   using C = Cfg<D>;
   constexpr int NCH = C::NCH;
   __shared__ __align__(16) unsigned char smem[C::SMEM];
@@ -165,11 +166,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   int nkeys = L, t0 = 0;
   long long kvbase = 0;
   if constexpr (KV) {
-    nkeys = kv_off + (n + 1) * L;
+    // kv_off < 0: a one-frame window, keys [n L, (n+1) L) (intra-frame only)
+    nkeys = kv_off < 0 ? L : kv_off + (n + 1) * L;
     const int nt_all = (nkeys + KT - 1) / KT;
     t0 = (int)((long long)sp * nt_all / nsplit);
     const int t1 = (int)((long long)(sp + 1) * nt_all / nsplit);
-    kvbase = (long long)b * Tk * ((long long)H * D) + (long long)h * D;
+    kvbase = ((long long)b * Tk + (kv_off < 0 ? (long long)n * L : 0)) * ((long long)H * D) + (long long)h * D;
     nkeys = (t1 == nt_all ? nkeys : t1 * KT) - t0 * KT;  // keys of this split
   }
   auto tile_rsrc = [&](const uint16_t* base, int j) {
@@ -433,13 +435,16 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     }
     const float inv = 1.f / lsum;
     uint16_t* op = out + fbase + (long long)my_q * H * D;
+    const float* ap = add_o ? add_o + fbase + (long long)my_q * H * D : nullptr;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const int dv = db * 32 + 8 * gg + 4 * hh;
-        st_global_8B(op + dv, u32x2{pack_bf16x2(o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv),
-                                    pack_bf16x2(o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv)});
+        f32x4 y = f32x4{o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv, o[db][4 * gg + 2] * inv,
+                        o[db][4 * gg + 3] * inv};
+        if (ap) y += *reinterpret_cast<const f32x4*>(ap + dv);  // the token-level inter-frame output
+        st_global_8B(op + dv, u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])});
       }
     }
     return;
@@ -590,7 +595,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                               (const uint16_t*)qp, states, stride_bh, stride_frame,
                               (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
-                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr);
+                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr);
   };
   if (s.d == 128) args(attn_bf16_kernel<128, false>);
   else args(attn_bf16_kernel<64, false>);
@@ -610,7 +615,7 @@ int kv_splits(const Shape& s, int kv_off) {
 
 hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v_cache, void* out, float* part_o,
                                void* part_ml, int nsplit, int Tk, int kv_off, const Shape& s, float scale,
-                               hipStream_t st) {
+                               hipStream_t st, const float* add_o) {
   const int qtiles = (s.L + QPB - 1) / QPB;
   const int units = s.B * s.H * s.F * nsplit;
   const int grid = ((units + 7) / 8) * 8 * qtiles;
@@ -618,7 +623,7 @@ hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
                               nullptr, 0, 0, nullptr, (uint16_t*)out, s.H, s.T, s.L, s.F, qtiles, units, c2, Tk,
-                              kv_off, nsplit, part_o, (float2*)part_ml);
+                              kv_off, nsplit, part_o, (float2*)part_ml, add_o);
   };
   if (s.d == 128) args(attn_bf16_kernel<128, true>);
   else args(attn_bf16_kernel<64, true>);

@@ -29,9 +29,20 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
 // nsplit * B * T * H float2) a merge pass adds up. kv_splits gives the split
 // count (shape only: equal shapes give bitwise equal results).
 int kv_splits(const Shape& s, int kv_off);
+// kv_off < 0 selects a one-frame window instead (keys of the query's own
+// frame: the intra-frame softmax without readout); with nsplit == 1, add_o
+// (fp32 [B, T, H, d], or null) is added to the output before it is rounded.
 hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v_cache, void* out, float* part_o,
                                void* part_ml, int nsplit, int Tk, int kv_off, const Shape& s, float scale,
-                               hipStream_t st);
+                               hipStream_t st, const float* add_o = nullptr);
+// Token-level access (token_level.hip): the per-token gated delta rule in
+// chunked form; writes the inter-frame output q'_t S_{t-1} (fp32 [B, T, H, d])
+// to o_inter and, with update_state, the final state. d = 128 only. frag holds
+// token_level_frag_bytes of per-chunk operands.
+size_t token_level_frag_bytes(const Shape& s);
+hipError_t launch_token_level(const void* qp, const void* kp, const void* vp, const float* alpha, const float* beta,
+                              float* state, void* frag, float* o_inter, int update_state, const Shape& s,
+                              hipStream_t st);
 // k, v [B, T, H, d] bf16 -> the cache [B, cache_tokens, H, d] at token at_token.
 hipError_t launch_kv_append(const void* k, const void* v, void* k_cache, void* v_cache, int cache_tokens,
                             int at_token, const Shape& s, hipStream_t st);

@@ -1,6 +1,6 @@
 // C ABI of the hybrid attention layer: argument validation, workspace layout
 // and launch order. The kernels live in attn_bf16.hip, state_bf16.hip,
-// state_scan.hip, fp32_path.hip, fmap.hip and gates.hip.
+// state_scan.hip, fp32_path.hip, fmap.hip, gates.hip and token_level.hip.
 //
 // Launch order of a call (ARL2 section 2.2: every token of frame N reads
 // S_{N-1}; the state is written once per clean frame, after the frame):
@@ -476,6 +476,60 @@ ha_status hybrid_attn_kvcache_forward(const void* q, const void* k, const void* 
   return launched(ha::launch_attn_kv_bf16(q, k_cache, v_cache, out, lay.total ? (float*)(ws + lay.part_o) : nullptr,
                                           lay.total ? (void*)(ws + lay.part_ml) : nullptr, lay.nsplit, cap,
                                           frame_index * frame_len, s, resolve_scale(softmax_scale, d), st));
+}
+
+}  // extern "C"
+
+// ---- token-level access (token_level.hip): the per-token gated delta rule
+// (prep + sequential chunk pass, writing the fp32 inter-frame output), then
+// the intra-frame softmax in its one-frame window, which adds that output
+// before rounding.
+namespace {
+size_t tl_frag_offset(const ha::Shape&) { return 0; }
+size_t tl_oint_offset(const ha::Shape& s) { return align_up(ha::token_level_frag_bytes(s)); }
+size_t tl_total(const ha::Shape& s) {
+  return tl_oint_offset(s) + align_up((size_t)s.B * s.T * s.H * (size_t)s.d * sizeof(float));
+}
+}  // namespace
+
+extern "C" {
+
+size_t hybrid_attn_token_level_workspace_bytes(int B, int H, int T, int frame_len, int d) {
+  ha::Shape s;
+  if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK || d != 128) return 0;
+  return tl_total(s);
+}
+
+ha_status hybrid_attn_forward_token_level(const void* q, const void* k, const void* v, const void* qp,
+                                          const void* kp, const void* vp, const float* alpha,
+                                          const float* beta, float* state, void* out, void* workspace,
+                                          size_t workspace_bytes, int B, int H, int T, int d, int frame_len,
+                                          ha_dtype dtype, int update_state, float softmax_scale, void* stream) {
+  ha::Shape s;
+  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  if (r != HA_OK) return r;
+  if (dtype != HA_BF16 || d != 128) return HA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !qp || !kp || !vp || !alpha || !beta || !state || !out || !workspace) return HA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qp, 16) || !aligned(kp, 16) ||
+      !aligned(vp, 16) || !aligned(state, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+      !aligned(alpha, 4) || !aligned(beta, 4))
+    return HA_ERR_ALIGN;
+  const size_t total = tl_total(s);
+  if (workspace_bytes < total) return HA_ERR_WORKSPACE;
+  const size_t tb = tensor_bytes(s, dtype);
+  const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
+  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) || overlap(out, tb, qp, tb) ||
+      overlap(out, tb, kp, tb) || overlap(out, tb, vp, tb) || overlap(out, tb, state, stb) ||
+      overlap(out, tb, workspace, total) || overlap(state, stb, workspace, total))
+    return HA_ERR_ALIAS;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* oint = (float*)(ws + tl_oint_offset(s));
+  if (ha::launch_token_level(qp, kp, vp, alpha, beta, state, ws + tl_frag_offset(s), oint, update_state, s, st) !=
+      hipSuccess)
+    return HA_ERR_DEVICE;
+  return launched(ha::launch_attn_kv_bf16(q, k, v, out, nullptr, nullptr, 1, T, -1, s,
+                                          resolve_scale(softmax_scale, d), st, oint));
 }
 
 }  // extern "C"
