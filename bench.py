@@ -5,7 +5,8 @@
 Variants (not the headline line): --variant fmap (per-head feature maps
 applied inside the call) and --variant gated (gates projected from the layer
 input x, maps, L2-normalised K'), each against the same prologue done by
-separate torch ops before hybrid_attn_forward.
+separate torch ops before hybrid_attn_forward; --variant token: token-level
+access (the per-token gated delta rule) against the frame-level layer.
 
 --baseline kvcache: the softmax teacher with a full KV cache against the
 hybrid layer, per streamed frame as the video grows (81 to 921 frames).
@@ -497,6 +498,57 @@ def bench_stack(args):
            "configs": rows}
     print(json.dumps(res), flush=True)
 
+
+def bench_token_level(w, args):
+    """Token-level access (per-token gated delta rule, chunked) against the
+    frame-level layer on the same inputs: one clean call over the workload."""
+    import torch
+    from video_dit_hybrid_amd import api
+    from video_dit_hybrid_amd import workloads as W
+    dev = torch.device("cuda:0")
+    log(f"bench: token-level variant, workload {w.name}: generating inputs")
+    inp = W.make_call_inputs(w, 0, w.frames, 0)
+    t = {k: W.as_torch(v, w.dtype if k in W.QKV_NAMES else "fp32", dev) for k, v in inp.items()}
+    s0 = torch.from_numpy(W.make_state0(w)).to(dev)
+    st = s0.clone()
+    out = torch.empty_like(t["q"])
+    ws = torch.empty(max(1, api.token_level_workspace_bytes(w.B, w.H, w.T, w.L, w.d)), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(max(1, api.workspace_bytes(w.B, w.H, w.T, w.L, w.d, 1)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def tok():
+        api.hybrid_attn_forward_token_level(t["q"], t["k"], t["v"], t["qp"], t["kp"], t["vp"], t["alpha"], t["beta"],
+                                            st, w.L, 1, out=out, workspace=ws)
+
+    def frm():
+        api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], t["kp"], t["vp"], t["alpha"], t["beta"], st, w.L, 1,
+                                out=out, workspace=ws2)
+
+    def ev_time(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_t = ev_time(tok)
+    ms_f = ev_time(frm)
+    res = {"metric": f"hybrid-attn frames/sec, {w.name} workload, token-level access (per-token gated delta rule), "
+                     "1 MI355X",
+           "value": round(w.B * w.frames / (ms_t / 1e3), 1), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_t, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{w.name} hybrid attention layer, token-level access", "B": w.B, "H": w.H,
+                      "d": w.d, "frames": w.frames, "frame_len": w.L, "tokens": w.T, "chunk": 64, "update_state": 1},
+           "frame_level": {"ms_per_step": round(ms_f, 4), "value": round(w.B * w.frames / (ms_f / 1e3), 1)},
+           "token_over_frame_time": round(ms_t / ms_f, 3)}
+    print(json.dumps(res), flush=True)
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -505,7 +557,7 @@ def main():
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "tiny", "stream", "batched"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--variant", choices=["plain", "fmap", "gated"], default="plain",
+    ap.add_argument("--variant", choices=["plain", "fmap", "gated", "token"], default="plain",
                     help="plain: the layer on given Q', K', V', alpha, beta (the headline); fmap / gated: the "
                          "prologue (maps; gates from x) inside the call, against an unfused torch prologue")
     ap.add_argument("--baseline", choices=["kvcache"], default=None,
@@ -538,7 +590,10 @@ def main():
         if w.frames_per_call or w.dtype != "bf16":
             print("--variant runs one bf16 clean call over a whole workload (480p, 720p)", file=sys.stderr)
             sys.exit(2)
-        bench_variant(w, args)
+        if args.variant == "token":
+            bench_token_level(w, args)
+        else:
+            bench_variant(w, args)
         return
     if w.frames_per_call:
         bench_streaming(w, args)

@@ -244,7 +244,15 @@ __global__ __launch_bounds__(256) void tl_prep_kernel(const uint16_t* __restrict
 // Per chunk: S to LDS as split B fragments; waves 0, 1 form X = U - W S for
 // token block w, waves 2, 3 Q S for token block w - 2; X to LDS as split B
 // fragments; waves 2, 3 write the inter-frame output c (Q S) + P X (fp32);
-// every wave advances its rows S = a S + K^T X.
+// every wave advances its rows S = a S + K^T X. The next chunk's operands are
+// loaded into registers while the current one computes (the barriers order
+// LDS only, so those loads stay in flight).
+struct TlOps {
+  u32x4 big[16];  // waves 0, 1: -W fragments [ks][hi/lo]; waves 2, 3: Q [ks] then P [ks][hi/lo]
+  f32x16 u;       // waves 0, 1: U block
+  u32x4 kk[4];    // K^T fragments of the wave's rows
+};
+
 __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __restrict__ frag,
                                                       const uint16_t* __restrict__ qp, const float* __restrict__ alpha,
                                                       float* __restrict__ state, float* __restrict__ o_inter,
@@ -261,16 +269,50 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
   for (int r = 0; r < 16; ++r) S[r] = Sg[(32 * w + 8 * (r >> 2) + 4 * hh + (r & 3)) * TLD + 32 * cb + lr];
   const size_t rs = (size_t)H * TLD;
   const int nc = F * nchf;
-  for (int c = 0; c < nc; ++c) {
+  const int tb = w & 1;
+
+  auto load = [&](int c, TlOps& o) {
     const int n = c / nchf, ci = c % nchf;
     const int t0 = n * L + ci * TLC;
     const int m = L - ci * TLC < TLC ? L - ci * TLC : TLC;
-    const float dec = ci == 0 ? alpha[((size_t)b * F + n) * H + h] : 1.0f;
     const unsigned char* fr = frag + ((size_t)bh * nc + c) * CHUNK_B;
     const u32x4* wf = reinterpret_cast<const u32x4*>(fr);
     const f32x4* uc = reinterpret_cast<const f32x4*>(fr + WF_B);
     const u32x4* pf = reinterpret_cast<const u32x4*>(fr + WF_B + UC_B);
     const u32x4* kf = reinterpret_cast<const u32x4*>(fr + WF_B + UC_B + PF_B);
+    if (w < 2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o.big[i] = wf[((tb * 8 + (i >> 1)) * 2 + (i & 1)) * 64 + lane];
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const f32x4 x = uc[((tb * 4 + cb) * 64 + lane) * 4 + v4];
+        o.u[4 * v4] = x[0]; o.u[4 * v4 + 1] = x[1]; o.u[4 * v4 + 2] = x[2]; o.u[4 * v4 + 3] = x[3];
+      }
+    } else {
+      const int i = 32 * tb + lr;
+      const uint16_t* qrow = qp + ((size_t)b * T + t0 + (i < m ? i : m - 1)) * rs + (size_t)h * TLD;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {  // Q rows, d in the permuted order of the S fragments
+        const int c0 = 16 * ks + 4 * hh;
+        const u32x2 q0 = *reinterpret_cast<const u32x2*>(qrow + c0);
+        const u32x2 q1 = *reinterpret_cast<const u32x2*>(qrow + c0 + 8);
+        o.big[ks] = u32x4{q0[0], q0[1], q1[0], q1[1]};
+      }
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) o.big[8 + i2] = pf[((tb * 4 + (i2 >> 1)) * 2 + (i2 & 1)) * 64 + lane];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) o.kk[ks] = kf[(w * 4 + ks) * 64 + lane];
+  };
+
+  TlOps cur, nxt;
+  load(0, cur);
+  for (int c = 0; c < nc; ++c) {
+    const int n = c / nchf, ci = c % nchf;
+    const int t0 = n * L + ci * TLC;
+    const int m = L - ci * TLC < TLC ? L - ci * TLC : TLC;
+    const float dec = ci == 0 ? alpha[((size_t)b * F + n) * H + h] : 1.0f;
+    if (c + 1 < nc) load(c + 1, nxt);
 
     // S -> LDS: registers [8s, 8s + 8) are the B operand of k-step 2w + s
 #pragma unroll
@@ -283,23 +325,16 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
       sfr[2 * w + s][0][lane] = hi;
       sfr[2 * w + s][1][lane] = lo;
     }
-    __syncthreads();
+    lds_barrier();
     f32x16 acc;
-    if (w < 2) {  // X = U - W S, token block w
-      const int tb = w;
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const f32x4 u = uc[((tb * 4 + cb) * 64 + lane) * 4 + v4];
-        acc[4 * v4] = u[0]; acc[4 * v4 + 1] = u[1]; acc[4 * v4 + 2] = u[2]; acc[4 * v4 + 3] = u[3];
-      }
+    if (w < 2) {  // X = U - W S, token block tb
+      acc = cur.u;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 ah = wf[((tb * 8 + ks) * 2 + 0) * 64 + lane];
-        const u32x4 al = wf[((tb * 8 + ks) * 2 + 1) * 64 + lane];
         const u32x4 sh = sfr[ks][0][lane], sl = sfr[ks][1][lane];
-        acc = mfma32x32x16(ah, sh, acc);
-        acc = mfma32x32x16(ah, sl, acc);
-        acc = mfma32x32x16(al, sh, acc);
+        acc = mfma32x32x16(cur.big[2 * ks], sh, acc);
+        acc = mfma32x32x16(cur.big[2 * ks], sl, acc);
+        acc = mfma32x32x16(cur.big[2 * ks + 1], sh, acc);
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -311,24 +346,16 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
         xfr[2 * tb + s][0][lane] = hi;
         xfr[2 * tb + s][1][lane] = lo;
       }
-    } else {  // Q S, token block w - 2 (Q rows in the permuted order over d)
-      const int tb = w - 2;
-      const int i = 32 * tb + lr;
-      const uint16_t* qrow = qp + ((size_t)b * T + t0 + (i < m ? i : m - 1)) * rs + (size_t)h * TLD;
+    } else {  // Q S, token block tb
       acc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int c0 = 16 * ks + 4 * hh;
-        const u32x2 q0 = *reinterpret_cast<const u32x2*>(qrow + c0);
-        const u32x2 q1 = *reinterpret_cast<const u32x2*>(qrow + c0 + 8);
-        const u32x4 qa = u32x4{q0[0], q0[1], q1[0], q1[1]};
-        acc = mfma32x32x16(qa, sfr[ks][0][lane], acc);
-        acc = mfma32x32x16(qa, sfr[ks][1][lane], acc);
+        acc = mfma32x32x16(cur.big[ks], sfr[ks][0][lane], acc);
+        acc = mfma32x32x16(cur.big[ks], sfr[ks][1][lane], acc);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (w >= 2) {  // out_i = c_i (Q S)_i + sum_{j<i} P_ij X_j
-      const int tb = w - 2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = 32 * tb + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -336,14 +363,11 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 ph = pf[((tb * 4 + ks) * 2 + 0) * 64 + lane];
-        const u32x4 pl = pf[((tb * 4 + ks) * 2 + 1) * 64 + lane];
         const u32x4 xh = xfr[ks][0][lane], xl = xfr[ks][1][lane];
-        acc = mfma32x32x16(ph, xh, acc);
-        acc = mfma32x32x16(ph, xl, acc);
-        acc = mfma32x32x16(pl, xh, acc);
+        acc = mfma32x32x16(cur.big[8 + 2 * ks], xh, acc);
+        acc = mfma32x32x16(cur.big[8 + 2 * ks], xl, acc);
+        acc = mfma32x32x16(cur.big[8 + 2 * ks + 1], xh, acc);
       }
-      // rows are tokens i, columns d = 32 cb + lr
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = 32 * tb + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -355,11 +379,11 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
     for (int r = 0; r < 16; ++r) S[r] *= dec;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 ka = kf[(w * 4 + ks) * 64 + lane];
-      S = mfma32x32x16(ka, xfr[ks][0][lane], S);
-      S = mfma32x32x16(ka, xfr[ks][1][lane], S);
+      S = mfma32x32x16(cur.kk[ks], xfr[ks][0][lane], S);
+      S = mfma32x32x16(cur.kk[ks], xfr[ks][1][lane], S);
     }
-    __syncthreads();
+    lds_barrier();
+    cur = nxt;
   }
   if (update_state) {
 #pragma unroll
