@@ -51,6 +51,8 @@ CLOCK_FILE = os.path.join(ROOT, "profiles", "attn_bf16_480p_clock.txt")
 PEAK_CLOCK_GHZ = 2.4        # the clock the published peak assumes
 # the attention kernel's sources: the counter summary is valid only for these exact bytes
 ATTN_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("attn_bf16.hip", "ha_device.h")]
+GATES_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("gates.hip", "ha_device.h")]
+GATES_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gates_480p_traffic.txt")
 
 
 def log(*a):
@@ -67,16 +69,17 @@ def flops(w):
     return att, rd, upd
 
 
-def attn_source_hash():
+def attn_source_hash(sources=None):
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in (ATTN_SOURCES if sources is None else sources):
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
-def profile_value(path, key):
-    """A number from a committed rocprofv3 summary of the attention kernel, or
-    None when the kernel's sources changed since the summary was taken."""
+def profile_value(path, key, sources=None):
+    """A number from a committed rocprofv3 summary of a kernel (the attention
+    kernel unless `sources` names others), or None when the kernel's sources
+    changed since the summary was taken."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -84,7 +87,7 @@ def profile_value(path, key):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != attn_source_hash():
+    if kv.get("kernel_source_sha256_16") != attn_source_hash(sources):
         return None
     try:
         return float(kv[key])
@@ -325,12 +328,98 @@ def bench_variant(w, args):
         torch.cuda.synchronize()
         gms = ev[0].elapsed_time(ev[1]) / args.steps
         gbytes = B * T * C * 2 + 2 * H * C * 2 + 2 * H * 4 + B * T * H * 4 + B * F * H * 4
-        res["gates_roofline"] = {"bound": "hbm", "achieved": round(gbytes / (gms / 1e3) / 1e9, 1),
-                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                 "frac": round(gbytes / (gms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                                 "kernel": "gates_kernel + alpha_kernel (hybrid_attn_gates)",
-                                 "bytes_per_launch": gbytes, "avg_launch_ms": round(gms, 4)}
+        traffic = profile_value(GATES_TRAFFIC_FILE, "traffic_bytes_per_launch", GATES_SOURCES) \
+            if w.name == "480p" else None
+        res["roofline"] = {"bound": "hbm", "achieved": round(gbytes / (gms / 1e3) / 1e9, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbytes / (gms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic,
+                           "kernel": "gates_kernel + alpha_kernel (hybrid_attn_gates), the row's new HBM-bound pass",
+                           "bytes_per_launch": gbytes, "avg_launch_ms": round(gms, 4)}
+    else:
+        res["roofline"] = attention_roofline(w, t, args.steps)
+    if not args.no_cpu:
+        log("bench: CPU oracle baseline")
+        res["cpu_baseline"] = variant_cpu_baseline(w, inp, mw, (x, g) if gated else None, s0.cpu().numpy(),
+                                                   args.cpu_budget)
     print(json.dumps(res), flush=True)
+
+
+def attention_roofline(w, t, steps):
+    """The attention kernel of a whole-workload call (intra-frame softmax +
+    readout, the dominant kernel of the fmap call too) timed alone with HIP
+    events on its stream, against the bf16 MFMA peak."""
+    import torch
+    from video_dit_hybrid_amd import api
+    dev = t["q"].device
+    snaps = torch.zeros((w.B, w.H, w.frames, w.d, w.d), dtype=torch.float32, device=dev)
+    out = torch.empty_like(t["q"])
+    qp = t.get("qp", t["q"])
+    stream = torch.cuda.current_stream(dev)
+
+    def one():
+        api.hybrid_attn_intra_readout(t["q"], t["k"], t["v"], qp, snaps, w.frames * w.d * w.d, w.d * w.d, w.L, out=out)
+    for _ in range(3):
+        one()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        one()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    att, rd, _ = flops(w)
+    tf = (att + rd) / (ms / 1e3) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for_current_kernel() if w.name == "480p" else None,
+            "kernel": "attn_bf16_kernel<128, false> (intra-frame softmax + readout)", "avg_launch_ms": round(ms, 4)}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # noqa: BLE001
+        return os.cpu_count() or 1
+
+
+def variant_cpu_baseline(w, inp, mw, gate, s0, budget_s):
+    """The fp64 oracle of the variant (feature maps, or gates + maps +
+    normalised keys, then the layer) on the first frames of the workload, all
+    heads, until budget_s elapses; frames/s."""
+    import oracle.hybrid_oracle as O
+    from video_dit_hybrid_amd import workloads as W
+    L = w.L
+    wx = {k: W.to_f64(W.from_torch(v, "bf16"), "bf16") for k, v in mw.items()}
+    if gate is not None:
+        x_t, g = gate
+        xg = W.to_f64(W.from_torch(x_t, "bf16"), "bf16")
+        wg, bg = W.to_f64(g["wgate"], "bf16"), g["bgate"].astype(np.float64)
+    S = [[s0[b, h].astype(np.float64) for h in range(w.H)] for b in range(w.B)]
+    done, el = 0, 0.0
+    for n in range(w.frames):
+        r = slice(n * L, (n + 1) * L)
+        x = {k: W.to_f64(inp[k][:, r], "bf16") for k in ("q", "k", "v")}
+        t0 = time.perf_counter()
+        if gate is not None:
+            a_n, b_n = O.gate_projections(xg[:, r], wg, bg, L)
+        else:
+            a_n, b_n = inp["alpha"][:, n:n + 1].astype(np.float64), inp["beta"][:, r].astype(np.float64)
+        qp, kp, vp = O.feature_maps(x["q"], x["k"], x["v"], wx["wq"], wx["wk"], wx["wv"], gate is not None)
+        for b in range(w.B):
+            for h in range(w.H):
+                O.intra_frame_attention(x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h])
+                O.inter_frame_readout(qp[b, :, h], S[b][h])
+                S[b][h] = O.delta_update(S[b][h], kp[b, :, h], vp[b, :, h], float(a_n[b, 0, h]), b_n[b, :, h])
+        el += time.perf_counter() - t0
+        done += 1
+        if el > budget_s:
+            break
+    return {"value": done * w.B / el, "unit": "frames/s", "cores": int(_threads()), "kind": "oracle",
+            "sample": f"first {done} of {w.frames} frames, all {w.B * w.H} (stream, head) pairs"
+                      + (", gate projections from x" if gate is not None else "") +
+                      ", per-head maps, intra softmax, readout and state update in fp64 numpy; "
+                      f"{el:.1f} s"}
 
 
 def bench_kvcache(args):
@@ -410,6 +499,7 @@ def bench_kvcache(args):
                       "kv_cache_bytes": 2 * lat * L * H * d * 2 * B, "hybrid_state_bytes": B * H * d * d * 4})
     n_last = samples[-1]
     flop_last = P * 4.0 * L * (n_last + 1) * L * d * H * B
+    tf_last = flop_last / (t_kv[n_last] / 1e3) / 1e12
     res = {"metric": "per-layer time of one streamed frame (4 denoise + 1 clean pass): KV-cache softmax teacher vs "
                      f"hybrid layer, 480p shape, frame {n_last}, 1 MI355X",
            "value": round(t_kv[n_last] / t_h, 2), "unit": "x (teacher time / hybrid time)", "n_gpus": 1,
@@ -418,8 +508,32 @@ def bench_kvcache(args):
                       "passes_per_frame": P},
            "hybrid_ms_per_frame": round(t_h, 4),
            "kv_cache_ms_per_frame": {str(n): round(t, 4) for n, t in t_kv.items()},
-           "kv_attention_tflops_at_last": round(flop_last / (t_kv[n_last] / 1e3) / 1e12, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tf_last, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf_last / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernel": f"attn_bf16_kernel<128, true> over {n_last + 1} frames of keys (whole passes: "
+                                  "cache append, attention, split merge)",
+                        "flop_per_frame": flop_last, "avg_frame_ms": round(t_kv[n_last], 4)},
            "video_curve": curve}
+    if not args.no_cpu:
+        import oracle.hybrid_oracle as O
+        n_cpu = min(20, nmax - 1)
+        log(f"bench: CPU oracle baseline (one pass of frame {n_cpu})")
+        q = W.to_f64(W.from_torch(passes[-1]["q"], "bf16"), "bf16")
+        kk = W.to_f64(W.from_torch(kc[:, :(n_cpu + 1) * L], "bf16"), "bf16")
+        vv = W.to_f64(W.from_torch(vc[:, :(n_cpu + 1) * L], "bf16"), "bf16")
+        t0 = time.perf_counter()
+        heads = 0
+        for h in range(H):
+            O.intra_frame_attention(q[0, :, h], kk[0, :, h], vv[0, :, h])
+            heads += 1
+            if time.perf_counter() - t0 > args.cpu_budget:
+                break
+        el = (time.perf_counter() - t0) * H / heads
+        res["cpu_baseline"] = {"value": round(1.0 / el, 4), "unit": f"passes/s at frame {n_cpu}", "cores": int(_threads()),
+                               "kind": "oracle", "sample": f"{heads} of {H} heads of one pass of frame {n_cpu} "
+                                                           f"({n_cpu + 1} frames of keys) in fp64 numpy, scaled to "
+                                                           f"all heads; GPU: {t_kv.get(n_cpu, float('nan')) / P:.3f} ms "
+                                                           "per pass" if n_cpu in t_kv else ""}
     print(json.dumps(res), flush=True)
 
 
@@ -547,6 +661,31 @@ def bench_token_level(w, args):
                       "d": w.d, "frames": w.frames, "frame_len": w.L, "tokens": w.T, "chunk": 64, "update_state": 1},
            "frame_level": {"ms_per_step": round(ms_f, 4), "value": round(w.B * w.frames / (ms_f / 1e3), 1)},
            "token_over_frame_time": round(ms_t / ms_f, 3)}
+    att, _, _ = flops(w)
+    inter = 6.0 * w.T * w.d * w.d * w.H * w.B  # per token: k'S, k'^T(v' - k'S), q'S
+    tf = (att + inter) / (ms_t / 1e3) / 1e12
+    res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                       "kernel": "whole call (tl_prep, tl_scan: the sequential chunk pass, 75 % of it; attention "
+                                 "in a one-frame window)", "flop_per_launch": att + inter, "avg_launch_ms": round(ms_t, 4)}
+    if not args.no_cpu:
+        import oracle.hybrid_oracle as O
+        log("bench: CPU oracle baseline (token-level, first frame)")
+        x = {k: W.to_f64(inp[k][:, :w.L], "bf16") for k in W.QKV_NAMES}
+        s0n = W.make_state0(w)
+        t0 = time.perf_counter()
+        heads = 0
+        for h in range(w.H):
+            O.hybrid_layer_token_level(x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h], x["qp"][0, :, h],
+                                       x["kp"][0, :, h], x["vp"][0, :, h], inp["alpha"][0, :1, h],
+                                       inp["beta"][0, :w.L, h].astype(np.float64), s0n[0, h].astype(np.float64), w.L, 1)
+            heads += 1
+            if time.perf_counter() - t0 > args.cpu_budget:
+                break
+        el = (time.perf_counter() - t0) * w.H / heads
+        res["cpu_baseline"] = {"value": round(w.B / el, 4), "unit": "frames/s", "cores": int(_threads()),
+                               "kind": "oracle", "sample": f"frame 0, {heads} of {w.H} heads (per-token loop in fp64 "
+                                                           "numpy, intra softmax), scaled to all heads"}
     print(json.dumps(res), flush=True)
 
 def main():
@@ -566,7 +705,7 @@ def main():
     ap.add_argument("--stack", action="store_true",
                     help="the 30-layer attention stack with 0/50/75/100 %% hybrid layers, streamed frames")
     ap.add_argument("--kv-frames", type=int, default=231, help="latent frames of the longest video (231 = 921 frames)")
-    ap.add_argument("--kernel", choices=["attn", "update", "copy"], default=None,
+    ap.add_argument("--kernel", choices=["attn", "update", "copy", "gates"], default=None,
                     help="launch only one phase (readout-only attention, or the state update) "
                          "steps times, for profilers; prints its average time")
     args = ap.parse_args()
@@ -597,6 +736,19 @@ def main():
         return
     if w.frames_per_call:
         bench_streaming(w, args)
+        return
+    if args.kernel == "gates":  # the gate pass alone, for profilers
+        dev = torch.device("cuda:0")
+        x = W.as_torch(W.make_layer_input(w, 0, w.frames, 0), "bf16", dev)
+        g = W.make_gate_weights(w)
+        wg, bg = W.as_torch(g["wgate"], "bf16", dev), W.as_torch(g["bgate"], "fp32", dev)
+        al = torch.empty((w.B, w.frames, w.H), dtype=torch.float32, device=dev)
+        be = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev)
+        gws = torch.empty(max(1, api.gates_workspace_bytes(w.B, w.H, w.T, w.L)), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup + args.steps):
+            api.hybrid_attn_gates(x, wg, bg, w.H, w.L, alpha=al, beta=be, workspace=gws)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": "gates", "workload": w.name, "launches": args.warmup + args.steps}), flush=True)
         return
     dev = torch.device("cuda:0")
     log(f"bench: workload {w.name}: generating inputs")
