@@ -51,7 +51,7 @@ CLOCK_FILE = os.path.join(ROOT, "profiles", "attn_bf16_480p_clock.txt")
 PEAK_CLOCK_GHZ = 2.4        # the clock the published peak assumes
 # the attention kernel's sources: the counter summary is valid only for these exact bytes
 ATTN_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("attn_bf16.hip", "ha_device.h")]
-GATES_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("gates.hip", "ha_device.h")]
+GATES_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("gates.hip", "ha_device.h", "ha_dma.h")]
 GATES_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gates_480p_traffic.txt")
 
 

@@ -19,6 +19,7 @@
 // accumulator registers [8s, 8s+8) of a 32x32 block are the operand of k-step
 // 2*(row band) + s.
 #include "ha_device.h"
+#include "ha_dma.h"
 #include "ha_gram_format.h"
 #include "ha_launch.h"
 
@@ -265,70 +266,135 @@ __global__ __launch_bounds__(D / 32 * 64) void mfrag_kernel(const float* __restr
 // and K'^T diag(beta) V' = W_k^T (K^T diag(beta / n) V) W_v, so the increment
 // pass keeps the unmapped K, V and takes two step-size vectors. This kernel
 // writes them: beta_g = beta / n^2, beta_b = beta / n.
-// One work-group (4 waves) per (b, 512-token chunk, head h): W_k of head h is
-// staged in LDS; wave w computes Y^T = W_k^T K^T for 128 tokens, one 32-token
-// column block at a time (A = W_k^T by transposed LDS reads, B = K^T straight
-// from the token-major K rows, the next block's rows loaded while the current
-// one computes), and n_t^2 is the column sum of squares of Y^T: its own
-// registers, then the other half-wave.
+// One work-group (4 waves) per (b, 512-token chunk, head h). Wave w owns the
+// output features [32 eb, 32 eb + 32) with eb = w % (D/32) and holds that
+// block of W_k^T as MFMA A fragments in registers for the whole chunk (read
+// once from a staging copy of W_k in LDS). The chunk's K rows stream through
+// LDS in slices of 64 tokens: direct global -> LDS copies of 1 KB per wave
+// instruction, each covering whole rows (4 x 256 bytes at d = 128), two
+// slices in flight while a third is read (deeper pipelines measured no
+// faster), chunk c of row r stored at position
+// c ^ kswz(r) so that the B operand reads (16 bytes of 16 consecutive rows per
+// LDS cycle) hit distinct banks. Per 32-token column block a wave forms its
+// 32 rows of Y^T = W_k^T K^T and their column sums of squares; the D/32 waves
+// sharing a column block add theirs through LDS in wave order.
+template <int NCH>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (NCH >= 16) return row & 15;
+  else return (row >> 1) & 7;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void keyscale_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ wk,
                                                        const float* __restrict__ beta,
                                                        float* __restrict__ beta_g, float* __restrict__ beta_b,
                                                        int H, int T, int nchunk) {
-  constexpr int NRB = D / 32, KS = D / 16, NTB = 4;  // 4 column blocks of 32 tokens per wave
-  __shared__ __align__(16) unsigned char wl[D * D * 2];
+  constexpr int RB = D * 2;              // bytes of one token's row of a head
+  constexpr int NCH = D / 8;             // 16-byte chunks per row
+  constexpr int KS = D / 16;             // MFMA k-steps over d
+  constexpr int NEB = D / 32;            // 32-feature blocks of Y^T
+  constexpr int TS = 64;                 // tokens per slice
+  constexpr int CT = 512;                // tokens per work-group
+  constexpr int SLICE = TS * RB;
+  constexpr int RPC = 1024 / RB;         // rows per 1 KB copy
+  constexpr int CPW = SLICE / 1024 / 4;  // copies per wave per slice
+  constexpr int NBUF = 3;                // slices in flight + 1
+  constexpr int TBW = 2 * NEB / 4;       // 32-token column blocks per wave and slice
+  static_assert(NBUF * SLICE >= D * D * 2, "W_k staging fits the slice buffers");
+  static_assert((NBUF - 2) * CPW <= 15, "vmcnt immediate");
+  __shared__ __align__(16) unsigned char smem[NBUF * SLICE];
+  __shared__ float part[2][NEB][TS];
   const int blk = blockIdx.x;
   const int h = blk % H, rest = blk / H;
   const int ch = rest % nchunk, b = rest / nchunk;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = ch * (4 * NTB * 32) + w * (NTB * 32) + lr;
-  auto load = [&](int tb, u32x4* kb) {
-    const int t = t0 + 32 * tb;
-    const uint16_t* kr = k + (((size_t)b * T + (t < T ? t : T - 1)) * H + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c0 = 16 * ks + 4 * hh;
-      const u32x2 k0 = *reinterpret_cast<const u32x2*>(kr + c0);
-      const u32x2 k1 = *reinterpret_cast<const u32x2*>(kr + c0 + 8);
-      kb[ks] = u32x4{k0[0], k0[1], k1[0], k1[1]};
-    }
-  };
-  u32x4 cur[KS], nxt[KS];
-  load(0, cur);
-  stage_w<D>(wl, wk + (size_t)h * D * D, tid, 256);
+  const int eb = w % NEB, tb0 = (w / NEB) * TBW;
+  const int ct0 = ch * CT;
+  const int ns = (T - ct0 < CT ? T - ct0 + TS - 1 : CT) / TS;  // slices of this chunk
+  const uint32_t rsb = (uint32_t)H * D * 2;  // bytes between consecutive tokens
+  const u32x4 rk = rsrc_words(k + ((size_t)b * T * H + h) * D, (int)((uint32_t)(T - 1) * rsb + RB));
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(smem));
+
+  // W_k^T rows 32 eb + lr, contraction d = 16 ks + 8 hh + j, into registers
+  {
+    const uint16_t* wh = wk + (size_t)h * D * D;
+    for (int i = tid; i < D * NCH; i += 256)
+      *reinterpret_cast<u32x4*>(smem + i * 16) = ld_global_16B(wh + (size_t)i * 8);
+  }
   __syncthreads();
-#pragma unroll
-  for (int tb = 0; tb < NTB; ++tb) {
-    if (tb + 1 < NTB) load(tb + 1, nxt);
-    f32x16 acc[NRB];
-#pragma unroll
-    for (int eb = 0; eb < NRB; ++eb) acc[eb] = f32x16{};
+  u32x4 wf[KS];
+  {
+    const uint16_t* wl = reinterpret_cast<const uint16_t*>(smem);
+    const int col = 32 * eb + lr;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int eb = 0; eb < NRB; ++eb) acc[eb] = mfma32x32x16(wtr<D>(wl, ks, eb, lane), cur[ks], acc[eb]);
-    float ss = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 16 * ks + 8 * hh + 2 * i;
+        wf[ks][i] = (uint32_t)wl[d0 * D + col] | ((uint32_t)wl[(d0 + 1) * D + col] << 16);
+      }
+  }
+  __syncthreads();  // the staging copy is consumed: the slices reuse its LDS
+
+  // copy s of a slice covers rows RPC s .. RPC s + RPC - 1: lane l fills
+  // position l % NCH of row RPC s + l / NCH; wave w issues copies w, w + 4, ...,
+  // whose rows have the same kswz for a given lane
+  const int crow = RPC * (w % (16 / RPC)) + lane / NCH;
+  const uint32_t voff = (uint32_t)(lane / NCH) * rsb + (uint32_t)(((lane % NCH) ^ kswz<NCH>(crow)) << 4);
+  auto issue = [&](int sl, int buf) {
+    const uint32_t base = lds0 + buf * SLICE;
+    const uint32_t t0 = (uint32_t)(ct0 + sl * TS);
 #pragma unroll
-    for (int eb = 0; eb < NRB; ++eb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ss = fmaf(acc[eb][r], acc[eb][r], ss);
-    ss += __shfl_xor(ss, 32);
-    const int t = t0 + 32 * tb;
-    if (hh == 0 && t < T) {
-      const float n2 = fmaxf(ss, 1e-24f);
-      const size_t i = ((size_t)b * T + t) * H + h;
-      const float be = beta[i];
-      beta_g[i] = be / n2;
-      beta_b[i] = be / sqrtf(n2);
+    for (int i = 0; i < CPW; ++i) {
+      const int sg = w + 4 * i;
+      dma16_asm(rk, base + sg * 1024, voff, (t0 + RPC * sg) * rsb);
     }
-    if (tb + 1 < NTB) {
+  };
+  // n_t^2 of the slice's tokens from the partial sums; token j by thread j
+  auto finish = [&](int sl) {
+    if (tid < TS) {
+      const int t = ct0 + sl * TS + tid;
+      float ss = part[sl & 1][0][tid];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
+      for (int e = 1; e < NEB; ++e) ss += part[sl & 1][e][tid];
+      if (t < T) {
+        const float n2 = fmaxf(ss, 1e-24f);
+        const size_t i = ((size_t)b * T + t) * H + h;
+        const float be = beta[i];
+        beta_g[i] = be / n2;
+        beta_b[i] = be / sqrtf(n2);
+      }
+    }
+  };
+
+  const int rd = (hh ^ kswz<NCH>(lr)) << 4;  // chunk 2 ks + hh of row 32 tb + lr: rd ^ (ks << 5)
+  for (int sl = 0; sl < NBUF - 1 && sl < ns; ++sl) issue(sl, sl);
+  for (int sl = 0; sl < ns; ++sl) {
+    // slice sl landed: at most the copies of the slices after it are outstanding
+    wait_later_copies<NBUF - 2, CPW>(ns - 1 - sl);
+    lds_barrier();  // all copies of slice sl are in LDS; slice sl-1 and its partial sums are consumed
+    if (sl + NBUF - 1 < ns) issue(sl + NBUF - 1, (sl + NBUF - 1) % NBUF);
+    if (sl > 0) finish(sl - 1);
+    const unsigned char* kt = smem + (sl % NBUF) * SLICE;
+#pragma unroll
+    for (int i = 0; i < TBW; ++i) {
+      const int tb = tb0 + i;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = mfma32x32x16(wf[ks], *reinterpret_cast<const u32x4*>(kt + (32 * tb + lr) * RB + (rd ^ (ks << 5))),
+                           acc);
+      float ss = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss = fmaf(acc[r], acc[r], ss);
+      ss += __shfl_xor(ss, 32);
+      if (hh == 0) part[sl & 1][eb][32 * tb + lr] = ss;
     }
   }
+  lds_barrier();
+  if (ns > 0) finish(ns - 1);
 }
 
 }  // namespace

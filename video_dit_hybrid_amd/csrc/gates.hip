@@ -7,33 +7,59 @@
 // The state is written once per frame, so frame N gets one forget gate, the
 // mean of its tokens' a_t; beta_t = g_t / L.
 //
-// The projection is a [tokens x C] x [C x 2H] product: on MFMA, with the 2H
-// gate rows as the A operand and 32 tokens as the B operand columns, both read
-// straight from global memory (C contiguous in both). The pass is bound by the
-// HBM read of x (2 bytes per token and channel); the weights (2H x C bf16)
-// stay in L2.
+// The projection is a [tokens x C] x [C x 2H] product on MFMA, the 2H gate
+// rows as the A operand and 32 tokens as the B operand columns. The pass is
+// bound by the HBM read of x (2 bytes per token and channel); the weights
+// (2H x C bf16) stay in L2.
 #include "ha_device.h"
+#include "ha_dma.h"
 #include "ha_launch.h"
 
 namespace ha {
 namespace {
 
-constexpr int GT = 64;  // tokens per work-group
+constexpr int GT = 64;          // tokens per work-group
+constexpr int SC = 64;          // channels per LDS slice
+constexpr int ROWB = SC * 2;    // bytes of one row's slice (8 chunks of 16 bytes)
+constexpr int RPC = 1024 / ROWB;  // rows per 1 KB copy
 
-// One work-group (4 waves) per (b, frame, 64-token chunk of the frame). Wave w
-// takes the k-steps ks = w, w + 4, ... of the C / 16 for both 32-token column
-// blocks, so each gate-weight fragment it loads serves 64 tokens; the four
-// partial logit blocks are added through LDS in wave order. Outputs: beta for
-// the chunk's tokens, and the chunk's sum of alpha gates per head (apart,
-// added up per frame by alpha_kernel).
+// LDS position of chunk c of slice row r: c ^ gswz(r). Sixteen consecutive rows
+// (one LDS cycle of 16-byte reads) then cover all 64 banks: rows of equal
+// parity share bank lines and get distinct positions.
+__device__ __forceinline__ int gswz(int row) { return (row >> 1) & 7; }
+
+// One work-group (4 waves) per (b, frame, 64-token chunk of the frame). The
+// chunk's x rows and the gate rows are streamed through LDS in slices of 64
+// channels: direct global -> LDS copies of 1 KB per wave instruction, each
+// covering 8 rows x 128 contiguous bytes (whole cache lines), two slices in
+// flight while a third is read (deeper pipelines measured no faster); the
+// small slices keep the LDS footprint at four work-groups per CU, so a 480p
+// launch (525 work-groups) runs in one round. In LDS a slice
+// is [row][8 chunks of 16 bytes] with chunk c of row r at position
+// c ^ gswz(r). Wave w takes k-step w of every slice for both 32-token column
+// blocks and all gate-row blocks; the four partial logit blocks are added through LDS
+// in wave order. x rows past the frame end and gate rows past 2H lie outside
+// their buffer descriptors and arrive as zeros. Outputs: beta for the chunk's
+// tokens, and the chunk's sum of alpha gates per head (apart, added up per
+// frame by alpha_kernel).
 template <int NOB>
 __global__ __launch_bounds__(256) void gates_kernel(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ wg,
                                                     const float* __restrict__ bg, float* __restrict__ beta,
                                                     float* __restrict__ apart, int T, int C, int H, int L,
                                                     int F, int nch) {
-  constexpr int UNR = NOB <= 2 ? 8 : 4;  // k-steps whose loads are issued together
-  __shared__ float red[4][NOB][2][16][64];
+  constexpr int NBUF = 3;                     // slices in flight + 1
+  constexpr int XT = GT * ROWB;               // x bytes of a slice
+  constexpr int WT = 32 * NOB * ROWB;         // gate-row bytes of a slice
+  constexpr int BUF = XT + WT;
+  constexpr int XSEG = XT / 1024 / 4;         // 1 KB copies per wave per slice: x
+  constexpr int WSEG = WT / 1024 / 4;         // and gate rows
+  constexpr int PER = XSEG + WSEG;
+  static_assert((NBUF - 2) * PER <= 15, "vmcnt immediate");
+  static_assert(SC / 16 == 4, "one k-step per wave and slice");
+  constexpr int RED = 4 * NOB * 2 * 16 * 64 * 4;  // partial logits of the 4 waves
+  constexpr int SMEM = NBUF * BUF > RED ? NBUF * BUF : RED;
+  __shared__ __align__(16) unsigned char smem[SMEM];
   __shared__ float sa[16 * NOB][GT];
   const int blk = blockIdx.x;
   const int c = blk % nch, bn = blk / nch;
@@ -41,54 +67,71 @@ __global__ __launch_bounds__(256) void gates_kernel(const uint16_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int O = 2 * H;
+  const int rows = L - c * GT < GT ? L - c * GT : GT;
+  const u32x4 rx = rsrc_words(x + ((size_t)b * T + (size_t)n * L + (size_t)c * GT) * C, rows * C * 2);
+  const u32x4 rw = rsrc_words(wg, O * C * 2);
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(smem));
 
-  // token rows of the two column blocks; the tail reads the frame's last token
-  const uint16_t* xr[2];
+  // copy s (rows 8s .. 8s + 7) of a slice: lane l fills position l % 8 of
+  // row 8s + l / 8; wave w issues copies w, w + 4, ..., whose rows have the
+  // same gswz for a given lane, so the per-lane offset is fixed
+  const int crow = RPC * (w & 1) + (lane >> 3);
+  const uint32_t voff = (uint32_t)(lane >> 3) * C * 2 + (uint32_t)(((lane & 7) ^ gswz(crow)) << 4);
+  auto issue = [&](int k, int buf) {
+    const uint32_t base = lds0 + buf * BUF;
+    const uint32_t ko = (uint32_t)k * ROWB;
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int tok = c * GT + 32 * tb + lr;
-    xr[tb] = x + ((size_t)b * T + (size_t)n * L + (tok < L ? tok : L - 1)) * C + 8 * hh;
-  }
-  const uint16_t* wr[NOB];
+    for (int i = 0; i < XSEG; ++i) {
+      const int sg = w + 4 * i;
+      dma16_asm(rx, base + sg * 1024, voff, (uint32_t)(RPC * sg) * C * 2 + ko);
+    }
 #pragma unroll
-  for (int ob = 0; ob < NOB; ++ob) {
-    const int o = 32 * ob + lr;  // rows past 2H repeat the last one; never stored
-    wr[ob] = wg + (size_t)(o < O ? o : O - 1) * C + 8 * hh;
-  }
+    for (int i = 0; i < WSEG; ++i) {
+      const int sg = w + 4 * i;
+      dma16_asm(rw, base + XT + sg * 1024, voff, (uint32_t)(RPC * sg) * C * 2 + ko);
+    }
+  };
+
   f32x16 acc[NOB][2];
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) acc[ob][0] = acc[ob][1] = f32x16{};
-  const int nks = C / 16;
-  for (int ks0 = w; ks0 < nks; ks0 += 4 * UNR) {
-    u32x4 xb[UNR][2], wa[UNR][NOB];
+  const int ns = (C + SC - 1) / SC;
+  const int rd = (hh ^ gswz(lr)) << 4;  // chunk 2ks + hh of row 32tb + lr: rd ^ (ks << 5)
+  for (int k = 0; k < NBUF - 1 && k < ns; ++k) issue(k, k);
+  for (int k = 0; k < ns; ++k) {
+    // slice k landed: at most the copies of the slices after it are outstanding
+    wait_later_copies<NBUF - 2, PER>(ns - 1 - k);
+    lds_barrier();  // every wave's copies of slice k are in LDS; slice k-1 is consumed
+    if (k + NBUF - 1 < ns) issue(k + NBUF - 1, (k + NBUF - 1) % NBUF);
+    const unsigned char* xs = smem + (k % NBUF) * BUF;
+    const unsigned char* wsl = xs + XT;
+    const int kv = (C - k * SC < SC ? C - k * SC : SC) / 16;  // k-steps of this slice
+    {
+      const int ks = w;
+      if (ks < kv) {
+        const int off = rd ^ (ks << 5);
+        u32x4 bx[2], aw[NOB];
 #pragma unroll
-    for (int i = 0; i < UNR; ++i) {
-      const int ks = ks0 + 4 * i;
-      if (ks < nks) {
+        for (int tb = 0; tb < 2; ++tb) bx[tb] = *reinterpret_cast<const u32x4*>(xs + (32 * tb + lr) * ROWB + off);
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) xb[i][tb] = ld_global_16B(xr[tb] + 16 * ks);
+        for (int ob = 0; ob < NOB; ++ob) aw[ob] = *reinterpret_cast<const u32x4*>(wsl + (32 * ob + lr) * ROWB + off);
 #pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) wa[i][ob] = ld_global_16B(wr[ob] + 16 * ks);
-      } else {
-        xb[i][0] = xb[i][1] = u32x4{0, 0, 0, 0};
+        for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) wa[i][ob] = u32x4{0, 0, 0, 0};
+          for (int tb = 0; tb < 2; ++tb) acc[ob][tb] = mfma32x32x16(aw[ob], bx[tb], acc[ob][tb]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < UNR; ++i)
-#pragma unroll
-      for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[ob][tb] = mfma32x32x16(wa[i][ob], xb[i][tb], acc[ob][tb]);
   }
+  lds_barrier();  // the slice buffers are free: they hold the partial logits next
+  float* red = reinterpret_cast<float*>(smem);
+  auto ridx = [&](int wv, int ob, int tb, int r, int ln) { return (((wv * NOB + ob) * 2 + tb) * 16 + r) * 64 + ln; };
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[w][ob][tb][r][lane] = acc[ob][tb][r];
-  __syncthreads();
+      for (int r = 0; r < 16; ++r) red[ridx(w, ob, tb, r, lane)] = acc[ob][tb][r];
+  lds_barrier();
 
   // logit (o, t) sits in register r = 4*(oo/8) + oo%4 of lane t%32 + 32*((oo/4)%2)
   // of block (o / 32, t / 32), oo = o % 32
@@ -97,10 +140,10 @@ __global__ __launch_bounds__(256) void gates_kernel(const uint16_t* __restrict__
     const int ob = o >> 5, oo = o & 31, tb = t >> 5;
     const int r = ((oo >> 3) << 2) | (oo & 3);
     const int ln = (t & 31) + 32 * ((oo >> 2) & 1);
-    const float z = red[0][ob][tb][r][ln] + red[1][ob][tb][r][ln] + red[2][ob][tb][r][ln] +
-                    red[3][ob][tb][r][ln] + bg[o];
+    const float z = red[ridx(0, ob, tb, r, ln)] + red[ridx(1, ob, tb, r, ln)] + red[ridx(2, ob, tb, r, ln)] +
+                    red[ridx(3, ob, tb, r, ln)] + bg[o];
     const float gsig = 1.0f / (1.0f + expf(-z));
-    const bool valid = c * GT + t < L;
+    const bool valid = t < rows;
     if (o >= H) {
       if (valid) beta[((size_t)b * T + (size_t)n * L + c * GT + t) * H + (o - H)] = gsig / (float)L;
     } else {

@@ -14,33 +14,12 @@
 // parts (hi = bf16(x), lo = bf16(x - hi)), which carries ~16 mantissa bits,
 // and both parts are accumulated on MFMA in fp32.
 #include "ha_device.h"
+#include "ha_dma.h"
 #include "ha_launch.h"
 #include "ha_gram_format.h"
 
 namespace ha {
 namespace {
-
-// global -> LDS copies issued from inline asm: the compiler cannot tell which
-// LDS buffer such a copy writes and would otherwise wait for every copy in
-// flight before each LDS read; completion is tracked by explicit vmcnt waits.
-// m0 holds the wave-uniform LDS destination.
-// s_nop 4: the compiler cannot see into the asm, and an SGPR operand it has
-// just written with a VALU instruction (v_readlane of a spilled SGPR) needs
-// five wait states before a VMEM read; m0 needs one.
-__device__ __forceinline__ void dma16_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
-}
-__device__ __forceinline__ void dma4_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
-}
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
-  const uint64_t a = (uint64_t)base;
-  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
-               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)),
-               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bytes), (uint32_t)kRsrcWord3};
-}
 
 constexpr int TC = 64;   // tokens per LDS chunk
 constexpr int NW = 8;    // waves per work-group

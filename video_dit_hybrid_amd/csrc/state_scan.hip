@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "ha_device.h"
+#include "ha_dma.h"
 #include "ha_launch.h"
 
 namespace ha {
@@ -28,15 +29,6 @@ namespace {
 
 // ---------------------------------------------------------------- bf16 path
 constexpr int CWM = 32;   // state columns per work-group
-
-// inline-asm global -> LDS copy (the compiler would otherwise order every
-// later LDS read behind it); completion is tracked by explicit vmcnt waits
-__device__ __forceinline__ void dma16_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-  // s_nop 4: an SGPR operand just written by a VALU instruction (a restored
-  // spill) needs five wait states before this VMEM read; m0 needs one
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
-}
 
 // Waves 0..NRB-1 compute (wave w: rows [32w, 32w+32) of the column block);
 // wave NRB only copies -G of the frames ahead into LDS, so the compute waves
