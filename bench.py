@@ -69,6 +69,15 @@ def flops(w):
     return att, rd, upd
 
 
+def update_bytes(w):
+    """Algorithmic HBM bytes of the state update per clean call: K', V' once
+    (2 L d elements each), beta (L) and alpha (1) per (stream, head, frame),
+    the state read once and one d x d fp32 state written per frame."""
+    hf = w.B * w.H * w.call_frames
+    el = 2 if w.dtype == "bf16" else 4
+    return hf * (2 * w.L * w.d * el + 4 * w.L + 4 + 4 * w.d * w.d) + w.B * w.H * 4 * w.d * w.d
+
+
 def attn_source_hash(sources=None):
     h = hashlib.sha256()
     for f in (ATTN_SOURCES if sources is None else sources):
@@ -814,26 +823,32 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    sev[0].record(stream)
+    for i in range(args.steps):
         step()
+        sev[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_ms = sorted(sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps))
 
     # dominant kernel alone: intra-frame attention + readout over all frames,
     # reading per-frame states (the snapshots the clean pass reads)
     snaps = torch.empty((w.B, w.H, w.frames, w.d, w.d), dtype=torch.float32, device=dev)
     st2 = torch.from_numpy(s0.copy()).to(dev)
     api.hybrid_attn_state_update(t["kp"], t["vp"], t["alpha"], t["beta"], st2, w.L, snapshots=snaps)
-    stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    lev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for _ in range(3):
         api.hybrid_attn_intra_readout(t["q"], t["k"], t["v"], t["qp"], snaps, w.frames * w.d * w.d,
                                       w.d * w.d, w.L, out=out)
     ev[0].record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         api.hybrid_attn_intra_readout(t["q"], t["k"], t["v"], t["qp"], snaps, w.frames * w.d * w.d,
                                       w.d * w.d, w.L, out=out)
+        lev[i].record(stream)
     ev[1].record(stream)
     gws = torch.empty(max(1, api.state_workspace_bytes(w.B, w.H, w.T, w.L, w.d)), dtype=torch.uint8, device=dev)
     for _ in range(args.steps):
@@ -843,6 +858,7 @@ def main():
     torch.cuda.synchronize()
     attn_ms = ev[0].elapsed_time(ev[1]) / args.steps
     upd_ms = ev[1].elapsed_time(ev[2]) / args.steps
+    launch_ms = sorted([ev[0].elapsed_time(lev[0])] + [lev[i].elapsed_time(lev[i + 1]) for i in range(args.steps - 1)])
 
     att, rd, upd = flops(w)
     total = att + rd + upd
@@ -852,7 +868,8 @@ def main():
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "kernel": "attn_bf16_kernel<128, false> (intra-frame softmax + Q'S readout)",
-            "flop_per_launch": att + rd, "avg_launch_ms": round(attn_ms, 4)}
+            "flop_per_launch": att + rd, "avg_launch_ms": round(attn_ms, 4),
+            "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4), "min_launch_ms": round(launch_ms[0], 4)}
     # The core clock under this kernel is well below the 2.4 GHz the peak
     # assumes. Its core-clock cycles per launch (rocprofv3 GRBM_GUI_ACTIVE, a
     # fixed amount of work) over this run's launch time give the clock of this
@@ -867,6 +884,7 @@ def main():
     metric = METRIC if w.name == "480p" else f"hybrid-attn frames/sec + % bf16 MFMA peak, {w.name} workload, 1 MI355X"
     res = {"metric": metric, "value": round(frames_s, 1), "unit": "frames/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "median_ms_per_step": round(step_ms[len(step_ms) // 2], 4), "min_ms_per_step": round(step_ms[0], 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
            "config": {"workload": f"{w.name} hybrid attention layer", "B": w.B, "H": w.H, "d": w.d,
@@ -876,7 +894,14 @@ def main():
            "layer_mfma_pct_of_peak": round(100 * total / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
            "algorithmic_gflop": {"attention": att / 1e9, "readout": rd / 1e9, "update": upd / 1e9},
            "kernel_ms": {"attention_readout": round(attn_ms, 4), "state_update": round(upd_ms, 4)},
-           "roofline": roof}
+           "roofline": roof,
+           "state_update": {"bound": "hbm", "achieved": round(update_bytes(w) / (upd_ms / 1e3) / 1e9, 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(update_bytes(w) / (upd_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                            "bytes_per_launch": update_bytes(w), "avg_launch_ms": round(upd_ms, 4),
+                            "tflops": round(upd / (upd_ms / 1e3) / 1e12, 2),
+                            "mfma_frac": round(upd / (upd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            "kernels": "gram + state scan (hybrid_attn_state_update, fp32 snapshots)"}}
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
         cb, worst, nf = cpu_baseline(w, inp, s0, first_out, args.cpu_budget)
