@@ -22,6 +22,19 @@ __device__ __forceinline__ void dma4_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t
   asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
 }
+// Four consecutive 1 KB copies (16 bytes per lane each) at instruction
+// offsets 0, 1024, 2048, 3072. The instruction offset moves both the global
+// address and the LDS destination (m0 + offset + 16 * lane), so one m0 /
+// soffset pair and one s_nop serve all four; they count as four vmcnt events.
+__device__ __forceinline__ void dma16x4_asm(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 4\n\t"
+               "buffer_load_dwordx4 %0, %1, %2 offen lds\n\t"
+               "buffer_load_dwordx4 %0, %1, %2 offen offset:1024 lds\n\t"
+               "buffer_load_dwordx4 %0, %1, %2 offen offset:2048 lds\n\t"
+               "buffer_load_dwordx4 %0, %1, %2 offen offset:3072 lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr) : "memory");
+}
+
 // Wait for the asm copies of the oldest slice in flight, when min(later, MAXL)
 // slices of PER copies each were issued after it and may stay in flight.
 // Loads retire in order, so vmcnt <= later * PER leaves exactly those.

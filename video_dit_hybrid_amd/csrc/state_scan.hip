@@ -45,6 +45,7 @@ __global__ __launch_bounds__((D / 32 + 1) * 64) void state_scan_mfma_kernel(
   constexpr size_t PER = (size_t)D * D * 8;         // workspace bytes per (b, h, frame)
   constexpr int GB = D * D * 4;                     // -G hi + lo bytes per frame
   constexpr int NSEG = GB / 1024;                   // 1 KB copies per frame
+  static_assert(NSEG % 4 == 0, "copies go in groups of four");
   // -G hi and lo fragments of two frames, then the S exchange (hi, lo; two frames)
   __shared__ __align__(16) unsigned char gbuf[2][GB];
   __shared__ __align__(16) u32x4 lds[2][2][KS][64];
@@ -66,9 +67,9 @@ __global__ __launch_bounds__((D / 32 + 1) * 64) void state_scan_mfma_kernel(
                            (uint32_t)kRsrcWord3};
     const uint32_t lds_g = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(&gbuf[0][0]));
     auto load = [&](int n) {
-#pragma unroll 8
-      for (int i = 0; i < NSEG; ++i)
-        dma16_asm(rs, lds_g + (n & 1) * GB + i * 1024, lane * 16, (uint32_t)((size_t)n * PER) + i * 1024);
+#pragma unroll 4
+      for (int i = 0; i < NSEG; i += 4)
+        dma16x4_asm(rs, lds_g + (n & 1) * GB + i * 1024, lane * 16, (uint32_t)((size_t)n * PER) + i * 1024);
     };
     // s_waitcnt immediate for "at most N vector-memory operations outstanding"
     // (vmcnt is 6 bits: N is capped at 63; expcnt and lgkmcnt left at their maxima)
