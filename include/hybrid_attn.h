@@ -194,7 +194,7 @@ size_t hybrid_attn_gated_workspace_bytes(int B, int H, int T, int frame_len, int
  * Q' = Q W_q, K' = K W_k, V' = V W_v, and with normalize_k != 0 each K' row
  * divided by max(||K'_t||_2, 1e-12) (no normalisation is named on the page;
  * unit keys are the delta rule's usual convention).
- *   x        [B, T, C] bf16, C channels per token (C % 16 == 0)
+ *   x        [B, T, C] bf16, C channels per token (C % 16 == 0, C < 2^23)
  *   w_gate   [2, H, C] bf16: row 0 the alpha projections, row 1 beta's
  *   b_gate   [2, H] fp32
  *   wq, wk, wv, q, k, v, state, out: as hybrid_attn_forward_fmap
@@ -224,7 +224,7 @@ size_t hybrid_attn_gates_workspace_bytes(int B, int H, int T, int frame_len);
  * alpha [B, F, H] and beta [B, T, H] (fp32) from x [B, T, C] bf16,
  * w_gate [2, H, C] bf16 and b_gate [2, H] fp32. alpha is the frame mean of
  * the per-token gates, summed in a fixed order (equal inputs give bitwise
- * equal results). bf16 only; C % 16 == 0; H <= 64. Outputs must not overlap
+ * equal results). bf16 only; C % 16 == 0, C < 2^23 (else HA_ERR_SHAPE); H <= 64. Outputs must not overlap
  * the inputs or the workspace (HA_ERR_ALIAS). Asynchronous on `stream`.
  */
 ha_status hybrid_attn_gates(const void* x, const void* w_gate, const float* b_gate,

@@ -148,7 +148,7 @@ def gated(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), 1), (dict(wg=None), 1), (dict(bg=None), 1), (dict(wk=None), 1), (dict(q=None), 1),
-    (dict(C=0), 2), (dict(C=24), 2), (dict(T=65), 2),
+    (dict(C=0), 2), (dict(C=24), 2), (dict(T=65), 2), (dict(C=1 << 23), 2),
     (dict(H=65), 3), (dict(dtype=1), 3), (dict(d=96), 3),
     (dict(x=4100), 4), (dict(wg=32772), 4), (dict(bg=36866), 4),
     (dict(ws_bytes=100), 5),
@@ -173,6 +173,7 @@ def test_gates_entry_validates():
         p = lambda v: None if v is None else P(v)
         return L.hybrid_attn_gates(p(x), p(wg), p(bg), p(al), p(be), p(ws), wsb, B, H, T, C, Lf, dtype, None)
     assert g(C=8) == 2 and g(T=65) == 2
+    assert g(C=1 << 23) == 2  # 64 tokens of C channels past 32-bit byte offsets
     assert g(al=None) == 1 and g(ws=None) == 1
     assert g(H=65) == 3 and g(dtype=1) == 3
     assert g(x=4097) == 4

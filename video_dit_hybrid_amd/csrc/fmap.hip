@@ -314,7 +314,10 @@ __global__ __launch_bounds__(256) void keyscale_kernel(const uint16_t* __restric
   const int ct0 = ch * CT;
   const int ns = (T - ct0 < CT ? T - ct0 + TS - 1 : CT) / TS;  // slices of this chunk
   const uint32_t rsb = (uint32_t)H * D * 2;  // bytes between consecutive tokens
-  const u32x4 rk = rsrc_words(k + ((size_t)b * T * H + h) * D, (int)((uint32_t)(T - 1) * rsb + RB));
+  // this chunk's rows of head h (at most CT tokens: 32-bit offsets for any T);
+  // rows past T are outside the range and arrive as zeros
+  const int crows = T - ct0 < CT ? T - ct0 : CT;
+  const u32x4 rk = rsrc_words(k + (((size_t)b * T + ct0) * H + h) * D, (int)((uint32_t)(crows - 1) * rsb + RB));
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(smem));
 
   // W_k^T rows 32 eb + lr, contraction d = 16 ks + 8 hh + j, into registers
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(256) void keyscale_kernel(const uint16_t* __restric
   const uint32_t voff = (uint32_t)(lane / NCH) * rsb + (uint32_t)(((lane % NCH) ^ kswz<NCH>(crow)) << 4);
   auto issue = [&](int sl, int buf) {
     const uint32_t base = lds0 + buf * SLICE;
-    const uint32_t t0 = (uint32_t)(ct0 + sl * TS);
+    const uint32_t t0 = (uint32_t)(sl * TS);  // relative to the chunk
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int sg = w + 4 * i;

@@ -282,6 +282,9 @@ ha_status fmap_run(const void* q, const void* k, const void* v, const void* wq, 
 // most 64 heads (2H gate rows in four 32-row MFMA blocks).
 ha_status check_gate_shape(const ha::Shape& s, int C) {
   if (C <= 0 || C % 16 != 0) return HA_ERR_SHAPE;
+  // 64 tokens (or 2H <= 128 gate rows) of C channels are addressed with
+  // 32-bit byte offsets
+  if ((long long)C * 2 * 128 > kMaxItems) return HA_ERR_SHAPE;
   if (s.H > 64) return HA_ERR_UNSUPPORTED;
   if ((long long)s.B * s.F * ha::gates_chunks(s) > kMaxItems) return HA_ERR_SHAPE;
   return HA_OK;
