@@ -63,10 +63,12 @@ def maps(w):
 
 
 @pytest.mark.parametrize("B,H,L,F,C", [(2, 12, 300, 3, 1536), (1, 3, 17, 3, 64), (1, 40, 100, 2, 256),
-                                       (1, 64, 64, 1, 128), (1, 12, 1560, 2, 1536)])
+                                       (1, 64, 64, 1, 128), (1, 12, 1560, 2, 1536), (2, 3, 50, 2, 16),
+                                       (1, 20, 100, 2, 80), (1, 13, 130, 2, 1552)])
 def test_gates_parity(B, H, L, F, C):
     """alpha (frame means) and beta against the oracle: one to four 32-row gate
-    blocks (H up to 64), ragged 32-token chunks, C from 64 to 1536."""
+    blocks (H up to 64), ragged 64-token chunks, C from 16 to 1552 (channel
+    counts that leave a partial last 64-channel slice: 16, 80, 1552)."""
     w = small("480p", B=B, H=H, L=L, frames=F, d=128)
     say(f"case gates B={B} H={H} L={L} F={F} C={C}")
     dev, ref = gate_case(w, C)
