@@ -719,8 +719,9 @@ def main():
                          "steps times, for profilers; prints its average time")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(heads and streams shard with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: heads and streams "
+              "shard over GPUs with no exchange inside the layer, and one GPU's share is what is timed",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -20,7 +20,7 @@ head h, for frame N with rows r = [N*L, (N+1)*L):
   clean-pass updates (2.2): denoising passes read S and never write it; only
       the clean pass writes it (update_state = 1).
 
-Readings where the page is silent or garbled (each is listed in the design doc):
+Readings where the page is silent or garbled:
   * the printed update rule has no transpose and no diag; the only
     dimensionally valid reading is K'^T diag(beta) (V' - K' S_{N-1}), with the
     residual taken against the undecayed S_{N-1} exactly as printed;
