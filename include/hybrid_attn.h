@@ -45,7 +45,8 @@ extern "C" {
 
 typedef enum {
   HA_BF16 = 0, /* q..vp and out are bfloat16 */
-  HA_FP32 = 1  /* q..vp and out are float32 */
+  HA_FP32 = 1, /* q..vp and out are float32 */
+  HA_DTYPE_MAX_ENUM = 0x7fffffff /* not a dtype: makes every int value representable */
 } ha_dtype;
 
 typedef enum {
@@ -56,7 +57,9 @@ typedef enum {
   HA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned (alpha, beta: 4-byte) */
   HA_ERR_WORKSPACE = 5,   /* workspace is NULL or smaller than the size the query returns */
   HA_ERR_DEVICE = 6,      /* a kernel launch failed */
-  HA_ERR_ALIAS = 7        /* out overlaps an input, the state, or the workspace */
+  HA_ERR_ALIAS = 7,       /* a buffer the call writes (out, state, snapshots, workspace)
+                             overlaps another buffer of the call */
+  HA_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes every int value representable */
 } ha_status;
 
 /*
@@ -85,7 +88,9 @@ size_t hybrid_attn_workspace_bytes(int B, int H, int T, int frame_len, int d,
  *   workspace    caller scratch of at least hybrid_attn_workspace_bytes(...)
  *   softmax_scale  s; a value <= 0 selects 1/sqrt(d)
  * When update_state is 0, kp, vp, alpha, beta and workspace may be NULL.
- * out must not overlap any input, the state or the workspace (HA_ERR_ALIAS).
+ * HA_ERR_ALIAS: out overlaps an input, the state or the workspace; or, with
+ * update_state != 0, the state or the workspace overlaps an input or each
+ * other (the workspace counted for the bytes the size query returns).
  */
 ha_status hybrid_attn_forward(const void* q, const void* k, const void* v,
                               const void* qp, const void* kp, const void* vp,
@@ -99,10 +104,12 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v,
 /*
  * The read side alone (ARL2 2.1 intra-frame branch plus the Q'S readout,
  * 2.2 frame-level access): out = softmax-within-frame(Q K^T s) V + Q' S_n for
- * every frame n, where S_n is the fp32 d x d matrix at
- *   states + b*state_stride_bh + n*state_stride_frame   (in floats).
+ * every frame n, where S_n of stream b and head h is the fp32 d x d matrix at
+ *   states + (b*H + h)*state_stride_bh + n*state_stride_frame   (in floats).
  * With state_stride_frame = 0 every frame reads the same state (a denoising
- * pass). Nothing but out is written.
+ * pass). Both strides are multiples of 4 floats (HA_ERR_ALIGN otherwise).
+ * Nothing but out is written; out must not overlap q, k, v, qp or the
+ * states (HA_ERR_ALIAS).
  */
 ha_status hybrid_attn_intra_readout(const void* q, const void* k,
                                     const void* v, const void* qp,
@@ -126,6 +133,8 @@ size_t hybrid_attn_state_workspace_bytes(int B, int H, int T, int frame_len,
  * 2.2 prescribes): state <- S_F after frames 0..F-1 of kp, vp, alpha, beta.
  * If snapshots is not NULL it receives S_{n-1} for every frame n, laid out
  * [B, H, F, d, d] fp32 (snapshot n of frame 0 is the input state).
+ * HA_ERR_ALIAS: state, snapshots or the workspace (counted for the bytes the
+ * size query returns) overlaps kp, vp, alpha, beta or one another.
  */
 ha_status hybrid_attn_state_update(const void* kp, const void* vp,
                                    const float* alpha, const float* beta,
@@ -301,8 +310,9 @@ ha_status hybrid_attn_forward_token_level(const void* q, const void* k, const vo
                                           ha_dtype dtype, int update_state,
                                           float softmax_scale, void* stream);
 
-/* A static, human-readable description of a status code. */
-const char* hybrid_attn_status_string(int status);
+/* A static, human-readable description of a status code ("unknown status"
+ * for a value that is not one). */
+const char* hybrid_attn_status_string(ha_status status);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int hybrid_attn_version(void);

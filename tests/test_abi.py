@@ -225,3 +225,71 @@ def test_token_level_workspace_and_validation():
     assert tl(q=4100) == 4
     assert tl(wsb=64) == 5
     assert tl(out=8192) == 7
+
+
+# Buffers 4 GiB apart, so no two overlap unless a case moves one onto another.
+SEP = dict(q=1 << 32, k=2 << 32, v=3 << 32, qp=4 << 32, kp=5 << 32, vp=6 << 32, alpha=7 << 32, beta=8 << 32,
+           state=9 << 32, out=10 << 32, ws=11 << 32, ws_bytes=1 << 40, d=96)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ws=SEP["q"] + 64), dict(ws=SEP["kp"]), dict(ws=SEP["beta"] + 16), dict(ws=SEP["state"] - 256),
+    dict(state=SEP["kp"] + 1024), dict(state=SEP["alpha"]), dict(state=SEP["q"]),
+    dict(out=SEP["state"] + 512), dict(out=SEP["ws"] + 4096),
+])
+def test_forward_rejects_written_buffers_that_overlap(kw):
+    # d = 96 would be HA_ERR_UNSUPPORTED; use d = 64 so the alias check is what
+    # decides (a call that passes every check would launch: none here does)
+    a = dict(SEP, d=64)
+    a.update(kw)
+    assert fwd(**a) == 7
+
+
+def test_forward_written_state_must_not_share_inputs():
+    # with update_state = 1 the state is written: overlapping q is rejected
+    # (a call that passed every check would launch, so the read-only case of
+    # update_state = 0 is covered by the GPU tests instead)
+    assert fwd(**dict(SEP, state=SEP["q"], update=1, d=64)) == 7
+
+
+def state_update(kp=1 << 32, vp=2 << 32, alpha=3 << 32, beta=4 << 32, state=5 << 32, snaps=6 << 32, ws=7 << 32,
+                 wsb=1 << 40, B=1, H=2, T=64, d=64, L=32):
+    p = lambda x: None if x is None else P(x)
+    return api.lib().hybrid_attn_state_update(p(kp), p(vp), p(alpha), p(beta), p(state), p(snaps), p(ws), wsb, B,
+                                              H, T, d, L, 0, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(snaps=1 << 32), dict(snaps=(2 << 32) + 4096), dict(snaps=(5 << 32) + 1024), dict(snaps=(7 << 32) + 256),
+    dict(ws=(1 << 32) + 16), dict(ws=(4 << 32)), dict(ws=(5 << 32) + 16384),
+    dict(state=(2 << 32) + 64), dict(state=3 << 32),
+])
+def test_state_update_rejects_written_buffers_that_overlap(kw):
+    assert state_update(**kw) == 7
+
+
+def test_state_update_snapshots_optional_and_sized_by_frames():
+    # snapshots [B, H, F, d, d] fp32: 2 frames x 2 heads x 16 KiB = 64 KiB, so
+    # a workspace 256 bytes before their end overlaps them
+    snap = 1 << 36
+    assert state_update(snaps=snap, ws=snap + 65536 - 256) == 7
+    # without snapshots: a state (2 heads x 16 KiB) reaching 256 bytes into the
+    # workspace
+    assert state_update(snaps=None, ws=5 << 32, state=(5 << 32) - 32768 + 256) == 7
+
+
+def test_feature_map_entry_rejects_workspace_over_inputs():
+    def fm(ws=9 << 32, update=1, state=7 << 32, d=64):
+        return api.lib().hybrid_attn_forward_fmap(P(1 << 32), P(2 << 32), P(3 << 32), P(4 << 32), P(5 << 32),
+                                                  P(6 << 32), P(10 << 32), P(11 << 32), P(state), P(8 << 32), P(ws),
+                                                  1 << 40, 1, 2, 64, d, 32, 0, update, 0.0, None)
+    assert fm(ws=(5 << 32) + 64) == 7           # workspace over wk
+    assert fm(ws=(11 << 32)) == 7               # workspace over beta
+    assert fm(state=2 << 32) == 7               # written state over k
+
+
+def test_status_string_of_every_status():
+    for code in range(8):
+        assert api.status_string(code) != "unknown status"
+    for code in (8, 99, -1, 2**31 - 1):
+        assert api.status_string(code) == "unknown status"

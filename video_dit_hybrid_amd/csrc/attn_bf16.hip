@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "ha_device.h"
+#include "ha_dma.h"
 #include "ha_launch.h"
 
 namespace ha {
@@ -158,8 +159,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   const long long fbase = ((long long)b * T + (long long)n * L) * ((long long)H * D) + (long long)h * D;
   // bytes of this (b, h, frame) slab as one buffer: tokens >= L read as zero
   const int span = (int)((uint32_t)(L - 1) * rsb + D * 2);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + fbase), 0, span, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + fbase), 0, span, kRsrcWord3);
+  const u32x4 rk = rsrc_words(k + fbase, span);
+  const u32x4 rv = rsrc_words(v + fbase, span);
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_ptr(smem));
   // KV mode: visible keys [0, nkeys) of the cache, this split's tiles
   // [t0, t0 + ntiles); each tile gets its own descriptor (32-bit offsets stay
   // inside one tile however long the cache)
@@ -176,8 +178,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   }
   auto tile_rsrc = [&](const uint16_t* base, int j) {
     const int rows = nkeys - j * KT < KT ? nkeys - j * KT : KT;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + kvbase + (long long)(t0 + j) * KT * H * D), 0,
-                                             (int)((uint32_t)(rows - 1) * rsb + D * 2), kRsrcWord3);
+    return rsrc_words(base + kvbase + (long long)(t0 + j) * KT * H * D, (int)((uint32_t)(rows - 1) * rsb + D * 2));
   };
 
   const int q0 = qt * QPB + wave * QPW;
@@ -199,19 +200,23 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     koff0 = row * rsb + ((pc ^ k_swz<NCH>(row)) << 4);
     voff0 = row * rsb + ((pc ^ v_swz<NCH>(row)) << 4);
   }
+  // The copies are inline asm: the compiler cannot tell which LDS bytes a
+  // builtin copy writes and would wait for every copy in flight before each
+  // later LDS read; with these, a tile's copies stay in flight until the wait
+  // at the end of the step.
   auto issue_k = [&](int j, int buf) {
     const uint32_t toff = KV ? 0u : (uint32_t)j * KT * rsb;
-    const __amdgpu_buffer_rsrc_t r = KV ? tile_rsrc(k, j) : rk;
+    const u32x4 r = KV ? tile_rsrc(k, j) : rk;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16_to_lds(r, kbuf + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
+      dma16_asm(r, lds0 + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
   };
   auto issue_v = [&](int j, int buf) {
     const uint32_t toff = KV ? 0u : (uint32_t)j * KT * rsb;
-    const __amdgpu_buffer_rsrc_t r = KV ? tile_rsrc(v, j) : rv;
+    const u32x4 r = KV ? tile_rsrc(v, j) : rv;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16_to_lds(r, vbuf + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
+      dma16_asm(r, lds0 + 2 * C::TILE + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
   };
 
   // ---- per-lane LDS read offsets
@@ -385,8 +390,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
         pv(vbuf + P * C::TILE, p0, p1);
       }
     }
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
   // flags: <P, NEXT, TAIL, LOADK>
   using Main0 = StepFlags<0, true, false, true>;
@@ -414,8 +421,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
         mt_a = tile_max(sa0, sa1);
       }
     }
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
 
   if constexpr (KV) {  // ---- epilogue without readout
@@ -459,8 +468,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
         make_rsrc(sfrag + (size_t)(b * H + h) * stride_bh + (size_t)n * stride_frame, D * D * 2);
 #pragma unroll
     for (int i = wave; i < NSEG; i += NW) dma16_to_lds(rs, smem + i * 1024, lane * 16, i * 1024);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if (!wave_active) return;
     const float inv = 1.f / sum_across_halves(l0 + l1);
 #pragma unroll

@@ -15,6 +15,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/hybrid_attn.h"
 #include "ha_launch.h"
 
@@ -55,6 +57,25 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// A buffer of a call: base pointer and the bytes the call may touch.
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// True when a buffer the call writes overlaps any other buffer of the call
+// (an input it reads, or another buffer it writes). NULL or empty spans are
+// absent arguments.
+bool written_overlaps(std::initializer_list<Span> written, std::initializer_list<Span> read) {
+  for (const Span* w = written.begin(); w != written.end(); ++w) {
+    for (const Span* o = written.begin(); o != written.end(); ++o)
+      if (o != w && overlap(w->p, w->n, o->p, o->n)) return true;
+    for (const Span& r : read)
+      if (overlap(w->p, w->n, r.p, r.n)) return true;
+  }
+  return false;
+}
+
 float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / sqrtf((float)d); }
 
 ha_status launched(hipError_t e) { return e == hipSuccess ? HA_OK : HA_ERR_DEVICE; }
@@ -85,7 +106,7 @@ extern "C" {
 
 int hybrid_attn_version(void) { return 100; }
 
-const char* hybrid_attn_status_string(int status) {
+const char* hybrid_attn_status_string(ha_status status) {
   switch (status) {
     case HA_OK: return "ok";
     case HA_ERR_NULL: return "a required pointer is NULL";
@@ -94,7 +115,7 @@ const char* hybrid_attn_status_string(int status) {
     case HA_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes; alpha and beta 4 bytes)";
     case HA_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case HA_ERR_DEVICE: return "a kernel launch failed";
-    case HA_ERR_ALIAS: return "out overlaps an input, the state or the workspace";
+    case HA_ERR_ALIAS: return "a buffer the call writes overlaps another buffer of the call";
     default: return "unknown status";
   }
 }
@@ -149,8 +170,15 @@ ha_status hybrid_attn_state_update(const void* kp, const void* vp, const float* 
   if (!aligned(kp, 16) || !aligned(vp, 16) || !aligned(state, 16) || !aligned(workspace, 16) ||
       !aligned(alpha, 4) || !aligned(beta, 4) || (snapshots && !aligned(snapshots, 16)))
     return HA_ERR_ALIGN;
-  if (workspace_bytes < hybrid_attn_state_workspace_bytes(B, H, T, frame_len, d))
-    return HA_ERR_WORKSPACE;
+  const size_t need = hybrid_attn_state_workspace_bytes(B, H, T, frame_len, d);
+  if (workspace_bytes < need) return HA_ERR_WORKSPACE;
+  const size_t tb = tensor_bytes(s, dtype);
+  const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
+  const size_t snb = snapshots ? stb * s.F : 0;
+  const size_t ab = (size_t)B * s.F * H * sizeof(float), bb = (size_t)B * T * H * sizeof(float);
+  if (written_overlaps({{state, stb}, {snapshots, snb}, {workspace, need}},
+                       {{kp, tb}, {vp, tb}, {alpha, ab}, {beta, bb}}))
+    return HA_ERR_ALIAS;
   return run_update(kp, vp, alpha, beta, state, snapshots, (float*)workspace, s, dtype,
                     (hipStream_t)stream);
 }
@@ -177,11 +205,14 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
 
   const size_t tb = tensor_bytes(s, dtype);
   const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
-  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
-      overlap(out, tb, qp, tb) || overlap(out, tb, state, stb) ||
-      (update_state && (overlap(out, tb, kp, tb) || overlap(out, tb, vp, tb) ||
-                        overlap(out, tb, workspace, need))))
+  const size_t ab = (size_t)B * s.F * H * sizeof(float), bb = (size_t)B * T * H * sizeof(float);
+  if (update_state) {
+    if (written_overlaps({{out, tb}, {state, stb}, {workspace, need}},
+                         {{q, tb}, {k, tb}, {v, tb}, {qp, tb}, {kp, tb}, {vp, tb}, {alpha, ab}, {beta, bb}}))
+      return HA_ERR_ALIAS;
+  } else if (written_overlaps({{out, tb}}, {{q, tb}, {k, tb}, {v, tb}, {qp, tb}, {state, stb}})) {
     return HA_ERR_ALIAS;
+  }
 
   const float scale = resolve_scale(softmax_scale, d);
   hipStream_t st = (hipStream_t)stream;
@@ -322,9 +353,14 @@ ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v, 
   const size_t tb = tensor_bytes(s, dtype);
   const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
   const size_t wb = (size_t)H * d * d * 2;
-  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
-      overlap(out, tb, wq, wb) || overlap(out, tb, state, stb) || overlap(out, tb, workspace, lay.total) ||
-      (update_state && (overlap(out, tb, wk, wb) || overlap(out, tb, wv, wb))))
+  const size_t ab = update_state ? (size_t)B * s.F * H * sizeof(float) : 0;
+  const size_t bb = update_state ? (size_t)B * T * H * sizeof(float) : 0;
+  const size_t uwb = update_state ? wb : 0;
+  if (update_state ? written_overlaps({{out, tb}, {state, stb}, {workspace, lay.total}},
+                                      {{q, tb}, {k, tb}, {v, tb}, {wq, wb}, {wk, uwb}, {wv, uwb}, {alpha, ab},
+                                       {beta, bb}})
+                   : written_overlaps({{out, tb}, {workspace, lay.total}},
+                                      {{q, tb}, {k, tb}, {v, tb}, {wq, wb}, {state, stb}}))
     return HA_ERR_ALIAS;
   return fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, (char*)workspace, lay, s, update_state,
                   resolve_scale(softmax_scale, d), (hipStream_t)stream);
@@ -363,10 +399,12 @@ ha_status hybrid_attn_forward_gated(const void* x, const void* q, const void* k,
   const size_t wb = (size_t)H * d * d * 2;
   const size_t xb = (size_t)B * T * (size_t)(update_state ? C : 0) * 2;
   const size_t gb = (size_t)2 * H * (size_t)(update_state ? C : 0) * 2;
-  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
-      overlap(out, tb, wq, wb) || overlap(out, tb, state, stb) || overlap(out, tb, workspace, lay.total) ||
-      (update_state && (overlap(out, tb, wk, wb) || overlap(out, tb, wv, wb) || overlap(out, tb, x, xb) ||
-                        overlap(out, tb, w_gate, gb) || overlap(out, tb, b_gate, (size_t)2 * H * 4))))
+  const size_t uwb = update_state ? wb : 0, bgb = update_state ? (size_t)2 * H * 4 : 0;
+  if (update_state ? written_overlaps({{out, tb}, {state, stb}, {workspace, lay.total}},
+                                      {{q, tb}, {k, tb}, {v, tb}, {wq, wb}, {wk, uwb}, {wv, uwb}, {x, xb},
+                                       {w_gate, gb}, {b_gate, bgb}})
+                   : written_overlaps({{out, tb}, {workspace, lay.total}},
+                                      {{q, tb}, {k, tb}, {v, tb}, {wq, wb}, {state, stb}}))
     return HA_ERR_ALIAS;
 
   char* ws = (char*)workspace;
@@ -521,9 +559,14 @@ ha_status hybrid_attn_forward_token_level(const void* q, const void* k, const vo
   if (workspace_bytes < total) return HA_ERR_WORKSPACE;
   const size_t tb = tensor_bytes(s, dtype);
   const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
-  if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) || overlap(out, tb, qp, tb) ||
-      overlap(out, tb, kp, tb) || overlap(out, tb, vp, tb) || overlap(out, tb, state, stb) ||
-      overlap(out, tb, workspace, total) || overlap(state, stb, workspace, total))
+  const size_t ab = (size_t)B * s.F * H * sizeof(float), bb = (size_t)B * T * H * sizeof(float);
+  // the state is written only with update_state; it is read either way
+  if (update_state ? written_overlaps({{out, tb}, {state, stb}, {workspace, total}},
+                                      {{q, tb}, {k, tb}, {v, tb}, {qp, tb}, {kp, tb}, {vp, tb}, {alpha, ab},
+                                       {beta, bb}})
+                   : written_overlaps({{out, tb}, {workspace, total}},
+                                      {{q, tb}, {k, tb}, {v, tb}, {qp, tb}, {kp, tb}, {vp, tb}, {alpha, ab},
+                                       {beta, bb}, {state, stb}}))
     return HA_ERR_ALIAS;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
