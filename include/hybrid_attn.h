@@ -59,6 +59,8 @@ typedef enum {
   HA_ERR_DEVICE = 6,      /* a kernel launch failed */
   HA_ERR_ALIAS = 7,       /* a buffer the call writes (out, state, snapshots, workspace)
                              overlaps another buffer of the call */
+  HA_ERR_SCRATCH = 8,     /* the call needs more workspace than hybrid_attn_forward_noalloc's
+                             fixed scratch holds (hybrid_attn_noalloc_scratch_bytes) */
   HA_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes every int value representable */
 } ha_status;
 
@@ -100,6 +102,32 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v,
                               int B, int H, int T, int d, int frame_len,
                               ha_dtype dtype, int update_state,
                               float softmax_scale, void* stream);
+
+/*
+ * hybrid_attn_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Arguments,
+ * results and errors are those of hybrid_attn_forward without the workspace:
+ * the call uses a fixed scratch array inside this library instead, of
+ * hybrid_attn_noalloc_scratch_bytes() bytes (64 MiB) on each GPU it runs on,
+ * held until the process ends. Calls whose workspace (the size
+ * hybrid_attn_workspace_bytes returns) exceeds it fail with HA_ERR_SCRATCH
+ * before any device work. The call allocates nothing and clears nothing (every
+ * scratch byte a call reads it has written first). All calls on one GPU share
+ * that GPU's scratch: two calls that overlap in time on one GPU (different
+ * streams, or different host threads without ordering) race and give wrong
+ * results; issue them on one stream. The stream must belong to the current
+ * device. HA_ERR_DEVICE also when the scratch address cannot be obtained.
+ */
+ha_status hybrid_attn_forward_noalloc(const void* q, const void* k, const void* v,
+                                      const void* qp, const void* kp, const void* vp,
+                                      const float* alpha, const float* beta,
+                                      float* state, void* out,
+                                      int B, int H, int T, int d, int frame_len,
+                                      ha_dtype dtype, int update_state,
+                                      float softmax_scale, void* stream);
+
+/* Bytes of scratch hybrid_attn_forward_noalloc holds per GPU. */
+size_t hybrid_attn_noalloc_scratch_bytes(void);
 
 /*
  * The read side alone (ARL2 2.1 intra-frame branch plus the Q'S readout,

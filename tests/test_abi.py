@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert api.lib().hybrid_attn_version() >= 100
-    for code in range(8):
+    for code in range(9):
         s = api.status_string(code)
         assert s and s != "unknown status"
     assert api.status_string(99) == "unknown status"
@@ -289,7 +289,34 @@ def test_feature_map_entry_rejects_workspace_over_inputs():
 
 
 def test_status_string_of_every_status():
-    for code in range(8):
+    for code in range(9):
         assert api.status_string(code) != "unknown status"
-    for code in (8, 99, -1, 2**31 - 1):
+    for code in (9, 99, -1, 2**31 - 1):
         assert api.status_string(code) == "unknown status"
+
+
+def noalloc(**kw):
+    a = dict(SEP, d=64, B=1, H=2, T=64, L=32, dtype=0, update=1, scale=0.0)
+    a.update(kw)
+    ptr = lambda x: None if x is None else P(x)
+    return api.lib().hybrid_attn_forward_noalloc(
+        ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["qp"]), ptr(a["kp"]), ptr(a["vp"]), ptr(a["alpha"]),
+        ptr(a["beta"]), ptr(a["state"]), ptr(a["out"]), a["B"], a["H"], a["T"], a["d"], a["L"], a["dtype"],
+        a["update"], a["scale"], None)
+
+
+def test_noalloc_entry_validates_before_touching_its_scratch():
+    assert api.noalloc_scratch_bytes() == 64 << 20
+    assert noalloc(q=None) == 1 and noalloc(alpha=None) == 1
+    assert noalloc(T=65) == 2 and noalloc(d=96) == 3 and noalloc(dtype=2) == 3
+    assert noalloc(q=SEP["q"] + 4) == 4
+    # a denoise pass needs no workspace, so the alias rules are checked without
+    # a scratch lookup
+    assert noalloc(update=0, out=SEP["k"] + 64) == 7
+    # the 720p 14B-shaped clean call needs 165 MiB of workspace: more than the
+    # fixed scratch holds
+    need = api.workspace_bytes(1, 40, 21 * 3600, 3600, 128, 1)
+    assert need > api.noalloc_scratch_bytes()
+    assert noalloc(H=40, T=21 * 3600, L=3600, d=128) == 8
+    # the 480p clean call fits
+    assert api.workspace_bytes(1, 12, 21 * 1560, 1560, 128, 1) <= api.noalloc_scratch_bytes()

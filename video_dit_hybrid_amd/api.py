@@ -12,14 +12,15 @@ import os
 
 HA_BF16, HA_FP32 = 0, 1
 STATUS = {0: "HA_OK", 1: "HA_ERR_NULL", 2: "HA_ERR_SHAPE", 3: "HA_ERR_UNSUPPORTED",
-          4: "HA_ERR_ALIGN", 5: "HA_ERR_WORKSPACE", 6: "HA_ERR_DEVICE", 7: "HA_ERR_ALIAS"}
+          4: "HA_ERR_ALIGN", 5: "HA_ERR_WORKSPACE", 6: "HA_ERR_DEVICE", 7: "HA_ERR_ALIAS", 8: "HA_ERR_SCRATCH"}
 EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_intra_readout",
            "hybrid_attn_state_update", "hybrid_attn_state_workspace_bytes",
            "hybrid_attn_status_string", "hybrid_attn_version", "hybrid_attn_forward_fmap",
            "hybrid_attn_fmap_workspace_bytes", "hybrid_attn_forward_gated",
            "hybrid_attn_gated_workspace_bytes", "hybrid_attn_gates", "hybrid_attn_gates_workspace_bytes",
            "hybrid_attn_kvcache_forward", "hybrid_attn_kvcache_workspace_bytes",
-           "hybrid_attn_forward_token_level", "hybrid_attn_token_level_workspace_bytes")
+           "hybrid_attn_forward_token_level", "hybrid_attn_token_level_workspace_bytes",
+           "hybrid_attn_forward_noalloc", "hybrid_attn_noalloc_scratch_bytes")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_attn.so")
 _lib = None
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.hybrid_attn_forward_token_level.restype = i
     L.hybrid_attn_token_level_workspace_bytes.argtypes = [i, i, i, i, i]
     L.hybrid_attn_token_level_workspace_bytes.restype = sz
+    L.hybrid_attn_forward_noalloc.argtypes = [vp] * 10 + [i, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_forward_noalloc.restype = i
+    L.hybrid_attn_noalloc_scratch_bytes.argtypes = []
+    L.hybrid_attn_noalloc_scratch_bytes.restype = sz
     L.hybrid_attn_status_string.argtypes = [i]
     L.hybrid_attn_status_string.restype = ctypes.c_char_p
     L.hybrid_attn_version.argtypes = []
@@ -123,6 +128,52 @@ def _check(name, t, shape, dtype, device):
 def _stream(device):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _forward_args(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, out):
+    """Checks of the forward call's tensors; returns (B, T, H, d, dtype code, out)."""
+    torch = _torch()
+    if q.device.type != "cuda":
+        raise ValueError("hybrid_attn_forward runs on a GPU; tensors must be on a cuda device")
+    B, T, H, d = q.shape
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    F = T // frame_len if frame_len > 0 and T % frame_len == 0 else -1
+    if F <= 0:
+        raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
+    for name, t in (("k", k), ("v", v), ("qp", qp)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    _check("state", state, (B, H, d, d), torch.float32, dev)
+    if update_state:
+        for name, t in (("kp", kp), ("vp", vp)):
+            _check(name, t, (B, T, H, d), dt, dev)
+        _check("alpha", alpha, (B, F, H), torch.float32, dev)
+        _check("beta", beta, (B, T, H), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, (B, T, H, d), dt, dev)
+    return B, T, H, d, code, out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().hybrid_attn_noalloc_scratch_bytes())
+
+
+def hybrid_attn_forward_noalloc(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, out,
+                                softmax_scale: float = 0.0):
+    """hybrid_attn_forward without a workspace argument: the library's fixed
+    per-GPU scratch is used instead, and nothing is allocated (out must be
+    given). Calls that overlap in time on one GPU race on that scratch."""
+    B, T, H, d, code, out = _forward_args(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, out)
+    st = lib().hybrid_attn_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(qp), _ptr(kp if update_state else None),
+        _ptr(vp if update_state else None), _ptr(alpha if update_state else None),
+        _ptr(beta if update_state else None), _ptr(state), _ptr(out), B, H, T, d, frame_len, code,
+        int(bool(update_state)), float(softmax_scale), _stream(q.device))
+    if st != 0:
+        raise HybridAttnError(st, "hybrid_attn_forward_noalloc")
+    return out
 
 
 def hybrid_attn_forward(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state,

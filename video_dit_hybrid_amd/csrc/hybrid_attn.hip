@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/hybrid_attn.h"
 #include "ha_launch.h"
@@ -100,6 +101,74 @@ ha_status run_update(const void* kp, const void* vp, const float* alpha, const f
   return launched(ha::launch_state_scan_fp32(gram, alpha, state, snaps, s, st));
 }
 
+// The arguments of a forward call other than its workspace and stream.
+struct ForwardArgs {
+  const void *q, *k, *v, *qp, *kp, *vp;
+  const float *alpha, *beta;
+  float* state;
+  void* out;
+  int B, H, T, d, frame_len;
+  ha_dtype dtype;
+  int update_state;
+  float softmax_scale;
+};
+
+// Checks of a forward call that do not involve the workspace; on success
+// fills the shape and the workspace bytes the call needs.
+ha_status validate_forward(const ForwardArgs& a, ha::Shape* s, size_t* need) {
+  ha_status r = check_shape(a.B, a.H, a.T, a.d, a.frame_len, a.dtype, s);
+  if (r != HA_OK) return r;
+  if (!a.q || !a.k || !a.v || !a.qp || !a.state || !a.out) return HA_ERR_NULL;
+  if (a.update_state && (!a.kp || !a.vp || !a.alpha || !a.beta)) return HA_ERR_NULL;
+  if (!aligned(a.q, 16) || !aligned(a.k, 16) || !aligned(a.v, 16) || !aligned(a.qp, 16) ||
+      !aligned(a.state, 16) || !aligned(a.out, 16))
+    return HA_ERR_ALIGN;
+  if (a.update_state &&
+      (!aligned(a.kp, 16) || !aligned(a.vp, 16) || !aligned(a.alpha, 4) || !aligned(a.beta, 4)))
+    return HA_ERR_ALIGN;
+  *need = hybrid_attn_workspace_bytes(a.B, a.H, a.T, a.frame_len, a.d, a.update_state);
+  return HA_OK;
+}
+
+// The aliasing rules of a forward call, with the workspace of `need` bytes.
+bool workspace_overlaps(const ForwardArgs& a, const ha::Shape& s, const void* ws, size_t need) {
+  const size_t tb = tensor_bytes(s, a.dtype);
+  const size_t stb = (size_t)a.B * a.H * (size_t)a.d * a.d * sizeof(float);
+  const size_t ab = (size_t)a.B * s.F * a.H * sizeof(float), bb = (size_t)a.B * a.T * a.H * sizeof(float);
+  if (a.update_state)
+    return written_overlaps({{a.out, tb}, {a.state, stb}, {ws, need}},
+                            {{a.q, tb}, {a.k, tb}, {a.v, tb}, {a.qp, tb}, {a.kp, tb}, {a.vp, tb}, {a.alpha, ab},
+                             {a.beta, bb}});
+  return written_overlaps({{a.out, tb}}, {{a.q, tb}, {a.k, tb}, {a.v, tb}, {a.qp, tb}, {a.state, stb}});
+}
+
+// Launch order of a validated forward call (see the top of this file).
+ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspace, hipStream_t st) {
+  const float scale = resolve_scale(a.softmax_scale, a.d);
+  const long long dd = (long long)a.d * a.d;
+  if (!a.update_state) return run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st);
+  float* gram = (float*)workspace;
+  if (s.F == 1) {
+    const ha_status r = run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st);
+    if (r != HA_OK) return r;
+    return run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st);
+  }
+  void* snap_area = (char*)workspace + align_up(ha::gram_bytes(s));
+  if (a.dtype == HA_BF16) {
+    // S_{n-1} of every frame as bf16 readout fragments (the readout rounds the
+    // state to bf16 either way)
+    const ha_status r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st, snap_area);
+    if (r != HA_OK) return r;
+    const long long fb = (long long)s.d * s.d * 2;  // fragment bytes per frame
+    return run_readout(a.q, a.k, a.v, a.qp, nullptr, (long long)s.F * fb, fb, a.out, s, a.dtype, scale, st,
+                       snap_area);
+  }
+  float* snaps = (float*)snap_area;
+  const ha_status r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, snaps, gram, s, a.dtype, st);
+  if (r != HA_OK) return r;
+  return run_readout(a.q, a.k, a.v, a.qp, snaps, (long long)s.F * dd, dd, a.out, s, a.dtype, scale, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,6 +185,7 @@ const char* hybrid_attn_status_string(ha_status status) {
     case HA_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case HA_ERR_DEVICE: return "a kernel launch failed";
     case HA_ERR_ALIAS: return "a buffer the call writes overlaps another buffer of the call";
+    case HA_ERR_SCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -189,56 +259,16 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
                               size_t workspace_bytes, int B, int H, int T, int d, int frame_len,
                               ha_dtype dtype, int update_state, float softmax_scale,
                               void* stream) {
+  const ForwardArgs a{q, k, v, qp, kp, vp, alpha, beta, state, out, B, H, T, d, frame_len, dtype, update_state,
+                      softmax_scale};
   ha::Shape s;
-  ha_status r = check_shape(B, H, T, d, frame_len, dtype, &s);
+  size_t need = 0;
+  ha_status r = validate_forward(a, &s, &need);
   if (r != HA_OK) return r;
-  if (!q || !k || !v || !qp || !state || !out) return HA_ERR_NULL;
-  if (update_state && (!kp || !vp || !alpha || !beta)) return HA_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qp, 16) ||
-      !aligned(state, 16) || !aligned(out, 16))
-    return HA_ERR_ALIGN;
-  if (update_state && (!aligned(kp, 16) || !aligned(vp, 16) || !aligned(alpha, 4) ||
-                       !aligned(beta, 4) || !aligned(workspace, 16)))
-    return HA_ERR_ALIGN;
-  const size_t need = hybrid_attn_workspace_bytes(B, H, T, frame_len, d, update_state);
+  if (update_state && !aligned(workspace, 16)) return HA_ERR_ALIGN;
   if (need > 0 && (!workspace || workspace_bytes < need)) return HA_ERR_WORKSPACE;
-
-  const size_t tb = tensor_bytes(s, dtype);
-  const size_t stb = (size_t)B * H * (size_t)d * d * sizeof(float);
-  const size_t ab = (size_t)B * s.F * H * sizeof(float), bb = (size_t)B * T * H * sizeof(float);
-  if (update_state) {
-    if (written_overlaps({{out, tb}, {state, stb}, {workspace, need}},
-                         {{q, tb}, {k, tb}, {v, tb}, {qp, tb}, {kp, tb}, {vp, tb}, {alpha, ab}, {beta, bb}}))
-      return HA_ERR_ALIAS;
-  } else if (written_overlaps({{out, tb}}, {{q, tb}, {k, tb}, {v, tb}, {qp, tb}, {state, stb}})) {
-    return HA_ERR_ALIAS;
-  }
-
-  const float scale = resolve_scale(softmax_scale, d);
-  hipStream_t st = (hipStream_t)stream;
-  const long long dd = (long long)d * d;
-  if (!update_state)
-    return run_readout(q, k, v, qp, state, dd, 0, out, s, dtype, scale, st);
-
-  float* gram = (float*)workspace;
-  if (s.F == 1) {
-    r = run_readout(q, k, v, qp, state, dd, 0, out, s, dtype, scale, st);
-    if (r != HA_OK) return r;
-    return run_update(kp, vp, alpha, beta, state, nullptr, gram, s, dtype, st);
-  }
-  void* snap_area = (char*)workspace + align_up(ha::gram_bytes(s));
-  if (dtype == HA_BF16) {
-    // S_{n-1} of every frame as bf16 readout fragments (the readout rounds the
-    // state to bf16 either way)
-    r = run_update(kp, vp, alpha, beta, state, nullptr, gram, s, dtype, st, snap_area);
-    if (r != HA_OK) return r;
-    const long long fb = (long long)s.d * s.d * 2;  // fragment bytes per frame
-    return run_readout(q, k, v, qp, nullptr, (long long)s.F * fb, fb, out, s, dtype, scale, st, snap_area);
-  }
-  float* snaps = (float*)snap_area;
-  r = run_update(kp, vp, alpha, beta, state, snaps, gram, s, dtype, st);
-  if (r != HA_OK) return r;
-  return run_readout(q, k, v, qp, snaps, (long long)s.F * dd, dd, out, s, dtype, scale, st);
+  if (workspace_overlaps(a, s, workspace, need)) return HA_ERR_ALIAS;
+  return launch_forward(a, s, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -576,6 +606,62 @@ ha_status hybrid_attn_forward_token_level(const void* q, const void* k, const vo
     return HA_ERR_DEVICE;
   return launched(ha::launch_attn_kv_bf16(q, k, v, out, nullptr, nullptr, 1, T, -1, s,
                                           resolve_scale(softmax_scale, d), st, oint));
+}
+
+}  // extern "C"
+
+// ---- allocation-free variant of hybrid_attn_forward, for callers that cannot
+// allocate (code under HIP graph capture, serving loops, harnesses that forbid
+// hipMalloc): the workspace is a fixed device array of this library instead of
+// a caller buffer. Every call on one GPU shares that GPU's copy.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;  // 64 MiB per GPU
+// The array's name is a host-side stand-in in host code: kernels get the
+// per-device address that hipGetSymbolAddress returns, never `scratch`.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+ha_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return HA_ERR_DEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hybrid_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+ha_status hybrid_attn_forward_noalloc(const void* q, const void* k, const void* v, const void* qp,
+                                      const void* kp, const void* vp, const float* alpha,
+                                      const float* beta, float* state, void* out, int B, int H, int T,
+                                      int d, int frame_len, ha_dtype dtype, int update_state,
+                                      float softmax_scale, void* stream) {
+  const ForwardArgs a{q, k, v, qp, kp, vp, alpha, beta, state, out, B, H, T, d, frame_len, dtype, update_state,
+                      softmax_scale};
+  ha::Shape s;
+  size_t need = 0;
+  ha_status r = validate_forward(a, &s, &need);
+  if (r != HA_OK) return r;
+  if (need > kScratchBytes) return HA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && (r = scratch_of_current_device(&ws)) != HA_OK) return r;
+  if (workspace_overlaps(a, s, ws, need)) return HA_ERR_ALIAS;
+  return launch_forward(a, s, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"
