@@ -204,6 +204,32 @@ def test_batch_permutation_permutes_outputs():
     assert torch.equal(stp, st[perm])
 
 
+def test_readout_with_frame_major_state_layout():
+    # states laid out [F, B, H, d, d]: S_n of (b, h) at (b*H + h)*d*d + n*B*H*d*d
+    w = small("480p", B=2, H=3, L=200, frames=3, state0_sigma=0.05)
+    say("case readout, frame-major state layout, B=2 H=3")
+    inp = W.make_call_inputs(w, 0, w.frames, 0)
+    dev = upload(inp, "bf16")
+    g = np.random.default_rng(7)
+    Sfb = (0.05 * g.standard_normal((w.frames, w.B, w.H, w.d, w.d))).astype(np.float32)
+    states = torch.from_numpy(Sfb).cuda()
+    out = api.hybrid_attn_intra_readout(dev["q"], dev["k"], dev["v"], dev["qp"], states,
+                                        w.d * w.d, w.B * w.H * w.d * w.d, w.L)
+    torch.cuda.synchronize()
+    got = W.to_f64(W.from_torch(out, "bf16"), "bf16")
+    x = f64(inp, "bf16")
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            for n in range(w.frames):
+                r = slice(n * w.L, (n + 1) * w.L)
+                ref = O.intra_frame_attention(x["q"][b, r, h], x["k"][b, r, h], x["v"][b, r, h]) + \
+                    O.inter_frame_readout(x["qp"][b, r, h], Sfb[n, b, h].astype(np.float64))
+                worst = max(worst, rel_err(got[b, r, h], ref))
+    say(f"frame-major states: rel_err out {worst:.3e}")
+    assert worst < TOL_OUT
+
+
 def test_sub_entry_points_compose_to_forward():
     w = small("480p", H=2, L=400, frames=3, state0_sigma=0.05)
     say("case sub entry points")
@@ -248,8 +274,10 @@ def _sampled_out_check(x, got, chains, w, samples, b=0):
 
 
 @pytest.mark.parametrize("name,heads,samples", [
-    ("480p", list(range(12)), [(0, 0), (1, 5), (10, 11), (20, 3), (20, 0)]),
-    ("720p", [0, 17, 39], [(0, 0), (11, 17), (20, 39)]),
+    # every head's final state; one output frame per head (frames spread over
+    # the call), plus the first and last frame of head 0
+    ("480p", list(range(12)), [((7 * h) % 21, h) for h in range(12)] + [(0, 0), (20, 0)]),
+    ("720p", list(range(40)), [((5 * h) % 21, h) for h in range(40)] + [(20, 0)]),
 ])
 def test_full_clean_pass_workloads(name, heads, samples):
     w = W.WORKLOADS[name]
@@ -341,13 +369,13 @@ def test_long_stream_constant_memory_and_parity():
                                 float(ci["alpha"][0, 0, h]), ci["beta"][0, :, h].astype(np.float64))
             hist.append(Sh)
         worst_s = max(worst_s, rel_err(S[0, h], Sh))
-        if h in (0, 11):
-            for f0, passes in keep.items():
-                for p, (inp, o) in passes.items():
-                    x = f64(inp, "bf16")
-                    ref = O.intra_frame_attention(x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h]) + \
-                        x["qp"][0, :, h] @ hist[f0]
-                    worst_o = max(worst_o, rel_err(W.to_f64(o[0, :, h], "bf16"), ref))
+        # every head: the first denoise pass and the clean pass of frames 0, 59, 119
+        for f0, passes in keep.items():
+            for p, (inp, o) in passes.items():
+                x = f64(inp, "bf16")
+                ref = O.intra_frame_attention(x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h]) + \
+                    x["qp"][0, :, h] @ hist[f0]
+                worst_o = max(worst_o, rel_err(W.to_f64(o[0, :, h], "bf16"), ref))
     say(f"stream: rel_err state {worst_s:.3e} after 120 frames (all heads), out {worst_o:.3e}")
     assert worst_s < TOL_STATE and worst_o < TOL_OUT
 
