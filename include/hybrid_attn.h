@@ -43,13 +43,20 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the enums below have int as their fixed underlying type, so every
+ * int a C caller passes is a valid value (C enums are ints already). */
+#ifdef __cplusplus
+#define HA_ENUM_INT : int
+#else
+#define HA_ENUM_INT
+#endif
+
+typedef enum HA_ENUM_INT {
   HA_BF16 = 0, /* q..vp and out are bfloat16 */
-  HA_FP32 = 1, /* q..vp and out are float32 */
-  HA_DTYPE_MAX_ENUM = 0x7fffffff /* not a dtype: makes every int value representable */
+  HA_FP32 = 1  /* q..vp and out are float32 */
 } ha_dtype;
 
-typedef enum {
+typedef enum HA_ENUM_INT {
   HA_OK = 0,
   HA_ERR_NULL = 1,        /* a required pointer is NULL */
   HA_ERR_SHAPE = 2,       /* a size <= 0, T % frame_len != 0, or a size too large to index */
@@ -59,9 +66,8 @@ typedef enum {
   HA_ERR_DEVICE = 6,      /* a kernel launch failed */
   HA_ERR_ALIAS = 7,       /* a buffer the call writes (out, state, snapshots, workspace)
                              overlaps another buffer of the call */
-  HA_ERR_SCRATCH = 8,     /* the call needs more workspace than hybrid_attn_forward_noalloc's
+  HA_ERR_SCRATCH = 8      /* the call needs more workspace than hybrid_attn_forward_noalloc's
                              fixed scratch holds (hybrid_attn_noalloc_scratch_bytes) */
-  HA_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes every int value representable */
 } ha_status;
 
 /*

@@ -72,5 +72,43 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return LIB_PATH
 
 
+SANITIZE_DIR = os.path.join(BUILD, "host_sanitized")
+SANITIZED_LIB = os.path.join(SANITIZE_DIR, "libhybrid_attn_host_sanitized.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer on every host function
+# (argument validation, workspace layout, grid math, launch order); the device
+# code is built as usual and never sanitized. The driver that uses this library
+# runs with no GPU visible, so its calls stop at failed launches.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g", "-O1"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Every source with ASan + UBSan on its host code, linked into a shared
+    library for the sanitizer driver (tests/abi_sanitizer_driver.c); returns its
+    path. Without a visible GPU the library's launches fail cleanly (HA_ERR_DEVICE)."""
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    cc = hipcc()
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+    def compile_one(src):
+        obj = os.path.join(SANITIZE_DIR, src.replace(".hip", ".o"))
+        cmd = [cc, f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", *SANITIZE_FLAGS,
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Wno-unused-command-line-argument", *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+        _run(cmd)
+        return obj
+
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+          "-fsanitize=undefined", "-shared-libsan", *objs, "-o", SANITIZED_LIB])
+    if verbose:
+        print("built", SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    if "--host-sanitized" in sys.argv:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose="-v" in sys.argv)

@@ -36,14 +36,17 @@ ha_status check_shape(int B, int H, int T, int d, int L, int dtype, ha::Shape* s
   if (T % L != 0) return HA_ERR_SHAPE;
   if (d != 64 && d != 128) return HA_ERR_UNSUPPORTED;
   if (dtype != HA_BF16 && dtype != HA_FP32) return HA_ERR_UNSUPPORTED;
+  // Each product below is bounded before the next factor joins it, so no
+  // intermediate overflows (every factor is < 2^31).
+  const long long F = T / L;
+  const long long bh = (long long)B * H;
+  if (bh > kMaxItems || bh * F * 2 > kMaxItems) return HA_ERR_SHAPE;
   // work items of the widest launch (fp32 readout: 64 queries per item)
-  const long long items = (long long)B * H * (T / L) * ((L + 63) / 64);
-  if (items > kMaxItems) return HA_ERR_SHAPE;
-  if ((long long)B * H * (T / L) * 2 > kMaxItems) return HA_ERR_SHAPE;
+  if (bh * F * (((long long)L + 63) / 64) > kMaxItems) return HA_ERR_SHAPE;
   // one (stream, head, frame) slab is addressed with 32-bit byte offsets, and
   // so are the per-frame state increments of one (stream, head)
-  if (((long long)L * H * d + d) * 4 > kMaxItems) return HA_ERR_SHAPE;
-  if ((long long)(T / L) * d * d * 8 > kMaxItems) return HA_ERR_SHAPE;
+  if ((long long)L * H > kMaxItems || ((long long)L * H * d + d) * 4 > kMaxItems) return HA_ERR_SHAPE;
+  if (F * d * d * 8 > kMaxItems) return HA_ERR_SHAPE;
   *s = ha::Shape{B, H, T, d, L, T / L};
   return HA_OK;
 }
@@ -511,6 +514,7 @@ extern "C" {
 size_t hybrid_attn_kvcache_workspace_bytes(int B, int H, int T, int frame_len, int d, int frame_index) {
   ha::Shape s;
   if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK || frame_index < 0) return 0;
+  if (((long long)frame_index + s.F) * frame_len > kMaxItems) return 0;  // cache tokens in 32 bits
   return kv_layout(s, frame_index).total;
 }
 
