@@ -66,9 +66,22 @@ typedef enum HA_ENUM_INT {
   HA_ERR_DEVICE = 6,      /* a kernel launch failed */
   HA_ERR_ALIAS = 7,       /* a buffer the call writes (out, state, snapshots, workspace)
                              overlaps another buffer of the call */
-  HA_ERR_SCRATCH = 8      /* the call needs more workspace than hybrid_attn_forward_noalloc's
+  HA_ERR_SCRATCH = 8,     /* the call needs more workspace than hybrid_attn_forward_noalloc's
                              fixed scratch holds (hybrid_attn_noalloc_scratch_bytes) */
+  HA_ERR_NONFINITE = 9    /* only with HA_CHECK_FINITE set: the state holds Inf or NaN after
+                             the call */
 } ha_status;
+
+/*
+ * Diagnostics, read from the environment at every call (any value other than
+ * empty or "0" switches one on):
+ *   HA_LOG           one line on stderr per call (sizes, workspace) and per
+ *                    kernel launch (grid, block, tiling).
+ *   HA_CHECK_FINITE  after every call that writes the state, a scan of it for
+ *                    Inf or NaN; the call then synchronises its stream and
+ *                    returns HA_ERR_NONFINITE if it finds one. This makes the
+ *                    call synchronous; not for use under HIP graph capture.
+ */
 
 /*
  * Bytes of workspace hybrid_attn_forward needs for these sizes: 0 when

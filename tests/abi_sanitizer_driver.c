@@ -31,7 +31,7 @@ static void expect(const char* what, int got, int want) {
 /* A status a call with no device may return: anything but success. */
 static void expect_error(const char* what, int got) {
   ++g_calls;
-  if (got <= HA_OK || got > HA_ERR_SCRATCH) {
+  if (got <= HA_OK || got > HA_ERR_NONFINITE) {
     fprintf(stderr, "FAIL %s: status %d is not an error code\n", what, got);
     g_fail = 1;
   }

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert api.lib().hybrid_attn_version() >= 100
-    for code in range(9):
+    for code in range(10):
         s = api.status_string(code)
         assert s and s != "unknown status"
     assert api.status_string(99) == "unknown status"
@@ -289,9 +289,9 @@ def test_feature_map_entry_rejects_workspace_over_inputs():
 
 
 def test_status_string_of_every_status():
-    for code in range(9):
+    for code in range(10):
         assert api.status_string(code) != "unknown status"
-    for code in (9, 99, -1, 2**31 - 1):
+    for code in (10, 99, -1, 2**31 - 1):
         assert api.status_string(code) == "unknown status"
 
 

@@ -12,7 +12,8 @@ import os
 
 HA_BF16, HA_FP32 = 0, 1
 STATUS = {0: "HA_OK", 1: "HA_ERR_NULL", 2: "HA_ERR_SHAPE", 3: "HA_ERR_UNSUPPORTED",
-          4: "HA_ERR_ALIGN", 5: "HA_ERR_WORKSPACE", 6: "HA_ERR_DEVICE", 7: "HA_ERR_ALIAS", 8: "HA_ERR_SCRATCH"}
+          4: "HA_ERR_ALIGN", 5: "HA_ERR_WORKSPACE", 6: "HA_ERR_DEVICE", 7: "HA_ERR_ALIAS", 8: "HA_ERR_SCRATCH",
+          9: "HA_ERR_NONFINITE"}
 EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_intra_readout",
            "hybrid_attn_state_update", "hybrid_attn_state_workspace_bytes",
            "hybrid_attn_status_string", "hybrid_attn_version", "hybrid_attn_forward_fmap",

@@ -52,6 +52,7 @@
 #include "ha_device.h"
 #include "ha_dma.h"
 #include "ha_launch.h"
+#include "ha_log.h"
 
 namespace ha {
 namespace {
@@ -602,6 +603,10 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
   const long long items = (long long)s.B * s.H * s.F * qtiles;
   const int grid = (int)((items + 7) / 8 * 8);
   const float c2 = scale * kLog2e;
+  HA_LOG("launch attn_bf16_kernel<%d>: grid %d x %d threads (%lld items = %d streams x %d heads x %d frames x %d "
+         "query tiles of %d; key tiles of %d, %d KiB LDS; readout from %s)",
+         s.d, grid, NT, items, s.B, s.H, s.F, qtiles, QPB, KT, (s.d == 128 ? Cfg<128>::SMEM : Cfg<64>::SMEM) >> 10,
+         sfrag ? "bf16 fragments" : "fp32 states");
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                               (const uint16_t*)qp, states, stride_bh, stride_frame,
@@ -631,6 +636,9 @@ hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v
   const int units = s.B * s.H * s.F * nsplit;
   const int grid = ((units + 7) / 8) * 8 * qtiles;
   const float c2 = scale * kLog2e;
+  HA_LOG("launch attn_bf16_kernel<%d, KV>: grid %d x %d threads (%d units x %d query tiles, %d key splits, keys "
+         "%s)%s", s.d, grid, NT, units, qtiles, nsplit, kv_off < 0 ? "of the own frame" : "of the cache",
+         nsplit > 1 ? " + attn_merge_kernel" : "");
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
                               nullptr, 0, 0, nullptr, (uint16_t*)out, s.H, s.T, s.L, s.F, qtiles, units, c2, Tk,
@@ -657,6 +665,7 @@ hipError_t launch_kv_append(const void* k, const void* v, void* k_cache, void* v
   const long long cap_b = (long long)cache_tokens * s.H * s.d * 2 / 16;
   const long long at = (long long)at_token * s.H * s.d * 2 / 16;
   const long long total = per_b * s.B;
+  HA_LOG("launch kv_append_kernel: %lld 16-byte pieces of K and V into the cache at token %d", total, at_token);
   kv_append_kernel<<<(int)((total + 255) / 256), 256, 0, st>>>((const u32x4*)k, (const u32x4*)v, (u32x4*)k_cache,
                                                               (u32x4*)v_cache, per_b, cap_b, at, total);
   return hipGetLastError();

@@ -22,6 +22,7 @@
 #include "ha_dma.h"
 #include "ha_gram_format.h"
 #include "ha_launch.h"
+#include "ha_log.h"
 
 namespace ha {
 namespace {
@@ -405,6 +406,7 @@ __global__ __launch_bounds__(256) void keyscale_kernel(const uint16_t* __restric
 hipError_t launch_gram_fmap(const float* partial, int nsplit, const void* wk, const void* wv, float* gram,
                             const Shape& s, hipStream_t st) {
   const int groups = s.B * s.H * s.F;
+  HA_LOG("launch gram_fmap_kernel<%d>: grid %d (sums of %d token splits, then the maps)", s.d, groups, nsplit);
   if (s.d == 128)
     gram_fmap_kernel<128><<<groups, 256, 0, st>>>(partial, nsplit, (const uint16_t*)wk, (const uint16_t*)wv,
                                                   gram, s.H, s.F);
@@ -418,6 +420,7 @@ hipError_t launch_mfrag(const float* states, long long sbh, long long sfr, const
                         const Shape& s, hipStream_t st) {
   const int ncb = s.d / 32;
   const int groups = s.B * s.H * frames * ncb;
+  HA_LOG("launch mfrag_kernel<%d>: grid %d (%d states per (b, h))", s.d, groups, frames);
   if (s.d == 128)
     mfrag_kernel<128><<<groups, 256, 0, st>>>(states, sbh, sfr, (const uint16_t*)wq, (u32x4*)mfrag, s.H, frames);
   else
@@ -429,6 +432,7 @@ hipError_t launch_keyscale(const void* k, const void* wk, const float* beta, flo
                            const Shape& s, hipStream_t st) {
   const int nchunk = (s.T + 511) / 512;
   const int grid = s.B * nchunk * s.H;
+  HA_LOG("launch keyscale_kernel<%d>: grid %d (512-token chunks)", s.d, grid);
   if (s.d == 128)
     keyscale_kernel<128><<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)wk, beta, beta_g, beta_b, s.H,
                                                s.T, nchunk);

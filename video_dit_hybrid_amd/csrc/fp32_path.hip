@@ -5,6 +5,7 @@
 // 2.2 frame-level access), computed with fp32 FMA and expf.
 #include "ha_device.h"
 #include "ha_launch.h"
+#include "ha_log.h"
 
 namespace ha {
 namespace {
@@ -155,6 +156,7 @@ hipError_t launch_attn_fp32(const void* q, const void* k, const void* v, const v
                             void* out, const Shape& s, float scale, hipStream_t st) {
   const int qtiles = (s.L + QB - 1) / QB;
   const long long items = (long long)s.B * s.H * s.F * qtiles;
+  HA_LOG("launch attn_fp32_kernel<%d>: grid %lld x %d threads (query tiles of %d)", s.d, items, NT_A, QB);
   auto go = [&](auto kern) {
     kern<<<(int)items, NT_A, 0, st>>>((const float*)q, (const float*)k, (const float*)v,
                                       (const float*)qp, states, stride_bh, stride_frame,
@@ -168,6 +170,7 @@ hipError_t launch_attn_fp32(const void* q, const void* k, const void* v, const v
 hipError_t launch_gram_fp32(const void* kp, const void* vp, const float* beta, float* gram,
                             const Shape& s, hipStream_t st) {
   const long long groups = (long long)s.B * s.H * s.F * 2;
+  HA_LOG("launch gram_fp32_kernel<%d>: grid %lld x %d threads", s.d, groups, NT_G);
   if (s.d == 128)
     gram_fp32_kernel<128><<<(int)groups, NT_G, 0, st>>>((const float*)kp, (const float*)vp, beta,
                                                         gram, s.H, s.T, s.L, s.F);

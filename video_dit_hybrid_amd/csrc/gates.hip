@@ -14,6 +14,7 @@
 #include "ha_device.h"
 #include "ha_dma.h"
 #include "ha_launch.h"
+#include "ha_log.h"
 
 namespace ha {
 namespace {
@@ -189,6 +190,7 @@ hipError_t launch_gates(const void* x, const void* wg, const float* bg, float* a
   const int nob = (2 * s.H + 31) / 32;
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* wp = (const uint16_t*)wg;
+  HA_LOG("launch gates_kernel<%d>: grid %d (%d 64-token chunks per frame, C = %d) + alpha_kernel", nob, grid, nch, C);
   switch (nob) {
     case 1: gates_kernel<1><<<grid, 256, 0, st>>>(xp, wp, bg, beta, apart, s.T, C, s.H, s.L, s.F, nch); break;
     case 2: gates_kernel<2><<<grid, 256, 0, st>>>(xp, wp, bg, beta, apart, s.T, C, s.H, s.L, s.F, nch); break;

@@ -13,15 +13,74 @@
 //                           on the snapshots (bf16 readout fragments on the
 //                           bf16 path, fp32 row-major on the fp32 path).
 #include <math.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <initializer_list>
 #include <mutex>
 
 #include "../../include/hybrid_attn.h"
 #include "ha_launch.h"
+#include "ha_log.h"
+
+namespace ha {
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+void log_line(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[hybrid_attn] %s\n", buf);
+}
+
+}  // namespace ha
 
 namespace {
+
+// ---- HA_CHECK_FINITE: a scan of a written state for Inf / NaN. The test is on
+// the exponent bits, which stays valid under -fno-honor-nans.
+__device__ unsigned int g_nonfinite;
+
+__global__ __launch_bounds__(256) void nonfinite_reset_kernel() { g_nonfinite = 0u; }
+
+__global__ __launch_bounds__(256) void nonfinite_scan_kernel(const float* __restrict__ x, long long n) {
+  bool bad = false;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    bad |= (__float_as_uint(x[i]) & 0x7f800000u) == 0x7f800000u;
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && (threadIdx.x & 63) == 0) atomicOr(&g_nonfinite, 1u);
+}
+
+// With HA_CHECK_FINITE set: scans nfloats floats at x after the work already on
+// st, synchronises st and reports what it found.
+ha_status check_finite(const char* what, const float* x, size_t nfloats, hipStream_t st) {
+  if (!ha::env_flag("HA_CHECK_FINITE") || nfloats == 0) return HA_OK;
+  const long long n = (long long)nfloats;
+  const int grid = (int)(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
+  nonfinite_reset_kernel<<<1, 1, 0, st>>>();
+  nonfinite_scan_kernel<<<grid, 256, 0, st>>>(x, n);
+  unsigned int found = 0;
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpyFromSymbol(&found, HIP_SYMBOL(g_nonfinite), sizeof found, 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return HA_ERR_DEVICE;
+  HA_LOG("HA_CHECK_FINITE: %s (%zu floats) %s", what, nfloats, found ? "holds Inf or NaN" : "finite");
+  return found ? HA_ERR_NONFINITE : HA_OK;
+}
+
+const char* dtype_name(int dtype) { return dtype == HA_BF16 ? "bf16" : dtype == HA_FP32 ? "fp32" : "?"; }
+
+void log_call(const char* entry, const ha::Shape& s, int dtype, int update_state, size_t workspace) {
+  HA_LOG("%s: B=%d H=%d T=%d (%d frames x %d tokens) d=%d %s update_state=%d workspace %zu bytes", entry, s.B, s.H,
+         s.T, s.F, s.L, s.d, dtype_name(dtype), update_state, workspace);
+}
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -151,25 +210,28 @@ ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspa
   const long long dd = (long long)a.d * a.d;
   if (!a.update_state) return run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st);
   float* gram = (float*)workspace;
+  const size_t nstate = (size_t)s.B * s.H * (size_t)dd;
   if (s.F == 1) {
-    const ha_status r = run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st);
+    ha_status r = run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st);
     if (r != HA_OK) return r;
-    return run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st);
+    r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st);
+    return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
   }
   void* snap_area = (char*)workspace + align_up(ha::gram_bytes(s));
   if (a.dtype == HA_BF16) {
     // S_{n-1} of every frame as bf16 readout fragments (the readout rounds the
     // state to bf16 either way)
-    const ha_status r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st, snap_area);
+    ha_status r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st, snap_area);
     if (r != HA_OK) return r;
     const long long fb = (long long)s.d * s.d * 2;  // fragment bytes per frame
-    return run_readout(a.q, a.k, a.v, a.qp, nullptr, (long long)s.F * fb, fb, a.out, s, a.dtype, scale, st,
-                       snap_area);
+    r = run_readout(a.q, a.k, a.v, a.qp, nullptr, (long long)s.F * fb, fb, a.out, s, a.dtype, scale, st, snap_area);
+    return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
   }
   float* snaps = (float*)snap_area;
-  const ha_status r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, snaps, gram, s, a.dtype, st);
+  ha_status r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, snaps, gram, s, a.dtype, st);
   if (r != HA_OK) return r;
-  return run_readout(a.q, a.k, a.v, a.qp, snaps, (long long)s.F * dd, dd, a.out, s, a.dtype, scale, st);
+  r = run_readout(a.q, a.k, a.v, a.qp, snaps, (long long)s.F * dd, dd, a.out, s, a.dtype, scale, st);
+  return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
 }
 
 }  // namespace
@@ -189,6 +251,7 @@ const char* hybrid_attn_status_string(ha_status status) {
     case HA_ERR_DEVICE: return "a kernel launch failed";
     case HA_ERR_ALIAS: return "a buffer the call writes overlaps another buffer of the call";
     case HA_ERR_SCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
+    case HA_ERR_NONFINITE: return "the state holds Inf or NaN after the call (HA_CHECK_FINITE)";
     default: return "unknown status";
   }
 }
@@ -228,6 +291,7 @@ ha_status hybrid_attn_intra_readout(const void* q, const void* k, const void* v,
   if (overlap(out, tb, q, tb) || overlap(out, tb, k, tb) || overlap(out, tb, v, tb) ||
       overlap(out, tb, qp, tb) || overlap(out, tb, states, sb))
     return HA_ERR_ALIAS;
+  log_call("hybrid_attn_intra_readout", s, dtype, 0, 0);
   return run_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame, out, s, dtype,
                      resolve_scale(softmax_scale, d), (hipStream_t)stream);
 }
@@ -252,8 +316,9 @@ ha_status hybrid_attn_state_update(const void* kp, const void* vp, const float* 
   if (written_overlaps({{state, stb}, {snapshots, snb}, {workspace, need}},
                        {{kp, tb}, {vp, tb}, {alpha, ab}, {beta, bb}}))
     return HA_ERR_ALIAS;
-  return run_update(kp, vp, alpha, beta, state, snapshots, (float*)workspace, s, dtype,
-                    (hipStream_t)stream);
+  log_call("hybrid_attn_state_update", s, dtype, 1, need);
+  r = run_update(kp, vp, alpha, beta, state, snapshots, (float*)workspace, s, dtype, (hipStream_t)stream);
+  return r != HA_OK ? r : check_finite("state", state, stb / sizeof(float), (hipStream_t)stream);
 }
 
 ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const void* qp,
@@ -271,6 +336,7 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
   if (update_state && !aligned(workspace, 16)) return HA_ERR_ALIGN;
   if (need > 0 && (!workspace || workspace_bytes < need)) return HA_ERR_WORKSPACE;
   if (workspace_overlaps(a, s, workspace, need)) return HA_ERR_ALIAS;
+  log_call("hybrid_attn_forward", s, dtype, update_state, need);
   return launch_forward(a, s, workspace, (hipStream_t)stream);
 }
 
@@ -339,7 +405,8 @@ ha_status fmap_run(const void* q, const void* k, const void* v, const void* wq, 
   if (ha::launch_gram_fmap(partial, nsplit, wk, wv, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
   if (ha::launch_state_scan_bf16(gram, alpha, state, snaps, nullptr, s, st) != hipSuccess) return HA_ERR_DEVICE;
   if (ha::launch_mfrag(snaps, (long long)s.F * dd, dd, wq, mf, s.F, s, st) != hipSuccess) return HA_ERR_DEVICE;
-  return run_readout(q, k, v, q, nullptr, (long long)s.F * fb, fb, out, s, HA_BF16, scale, st, mf);
+  const ha_status r = run_readout(q, k, v, q, nullptr, (long long)s.F * fb, fb, out, s, HA_BF16, scale, st, mf);
+  return r != HA_OK ? r : check_finite("state", state, (size_t)s.B * s.H * (size_t)dd, st);
 }
 
 // Shape checks of the gate projection: C channels in 16-element k-steps, at
@@ -395,6 +462,7 @@ ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v, 
                    : written_overlaps({{out, tb}, {workspace, lay.total}},
                                       {{q, tb}, {k, tb}, {v, tb}, {wq, wb}, {state, stb}}))
     return HA_ERR_ALIAS;
+  log_call("hybrid_attn_forward_fmap", s, dtype, update_state, lay.total);
   return fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, (char*)workspace, lay, s, update_state,
                   resolve_scale(softmax_scale, d), (hipStream_t)stream);
 }
@@ -443,6 +511,7 @@ ha_status hybrid_attn_forward_gated(const void* x, const void* q, const void* k,
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   const float scale = resolve_scale(softmax_scale, d);
+  log_call("hybrid_attn_forward_gated", s, dtype, update_state, lay.total);
   if (!update_state)
     return fmap_run(q, k, v, wq, wk, wv, nullptr, nullptr, nullptr, state, out, ws, lay, s, 0, scale, st);
   float* alpha = (float*)(ws + lay.alpha);
@@ -484,6 +553,7 @@ ha_status hybrid_attn_gates(const void* x, const void* w_gate, const float* b_ga
       overlap(beta, bb, workspace, wsb) || overlap(alpha, ab, b_gate, (size_t)2 * H * 4) ||
       overlap(beta, bb, b_gate, (size_t)2 * H * 4))
     return HA_ERR_ALIAS;
+  log_call("hybrid_attn_gates", s, dtype, 0, wsb);
   return launched(ha::launch_gates(x, w_gate, b_gate, alpha, beta, (float*)workspace, C, s, (hipStream_t)stream));
 }
 
@@ -545,6 +615,7 @@ ha_status hybrid_attn_kvcache_forward(const void* q, const void* k, const void* 
     return HA_ERR_ALIAS;
   hipStream_t st = (hipStream_t)stream;
   const int cap = cache_frames * frame_len;
+  log_call("hybrid_attn_kvcache_forward", s, dtype, 0, lay.total);
   if (ha::launch_kv_append(k, v, k_cache, v_cache, cap, frame_index * frame_len, s, st) != hipSuccess)
     return HA_ERR_DEVICE;
   char* ws = (char*)workspace;
@@ -605,11 +676,13 @@ ha_status hybrid_attn_forward_token_level(const void* q, const void* k, const vo
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   float* oint = (float*)(ws + tl_oint_offset(s));
+  log_call("hybrid_attn_forward_token_level", s, dtype, update_state, total);
   if (ha::launch_token_level(qp, kp, vp, alpha, beta, state, ws + tl_frag_offset(s), oint, update_state, s, st) !=
       hipSuccess)
     return HA_ERR_DEVICE;
-  return launched(ha::launch_attn_kv_bf16(q, k, v, out, nullptr, nullptr, 1, T, -1, s,
-                                          resolve_scale(softmax_scale, d), st, oint));
+  r = launched(ha::launch_attn_kv_bf16(q, k, v, out, nullptr, nullptr, 1, T, -1, s, resolve_scale(softmax_scale, d),
+                                       st, oint));
+  return r != HA_OK || !update_state ? r : check_finite("state", state, stb / sizeof(float), st);
 }
 
 }  // extern "C"
@@ -665,6 +738,7 @@ ha_status hybrid_attn_forward_noalloc(const void* q, const void* k, const void* 
   void* ws = nullptr;
   if (need > 0 && (r = scratch_of_current_device(&ws)) != HA_OK) return r;
   if (workspace_overlaps(a, s, ws, need)) return HA_ERR_ALIAS;
+  log_call("hybrid_attn_forward_noalloc", s, dtype, update_state, need);
   return launch_forward(a, s, ws, (hipStream_t)stream);
 }
 

@@ -16,6 +16,7 @@
 #include "ha_device.h"
 #include "ha_dma.h"
 #include "ha_launch.h"
+#include "ha_log.h"
 #include "ha_gram_format.h"
 
 namespace ha {
@@ -299,6 +300,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float* beta, const float* beta2,
                                      float* partial, int nsplit, const Shape& s, hipStream_t st) {
   const int grid = (int)((long long)s.B * s.H * s.F * nsplit);
+  HA_LOG("launch gram_bf16_kernel<%d> (partial sums): grid %d x %d threads (%d token splits per frame%s)", s.d, grid,
+         NT, nsplit, beta2 ? ", two step-size vectors" : "");
   auto run = [&](auto gk) {
     gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, beta2, nullptr, partial, nsplit, s.H,
                             s.T, s.L, s.F);
@@ -320,6 +323,8 @@ hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, f
   // partial sums after the increments (gram_bytes reserves both)
   float* partial = nsplit > 1 ? gram + gram_final_bytes(s) / sizeof(float) : nullptr;
   const int grid = (int)(groups * nsplit);
+  HA_LOG("launch gram_bf16_kernel<%d>: grid %d x %d threads (%lld (b,h,frame) x %d token splits)%s", s.d, grid, NT,
+         groups, nsplit, nsplit > 1 ? " + gram_reduce_kernel" : "");
   auto run = [&](auto gk, auto rk, int nrb) {
     gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, nullptr, gram, partial, nsplit,
                             s.H, s.T, s.L, s.F);

@@ -23,6 +23,7 @@
 #include "ha_device.h"
 #include "ha_dma.h"
 #include "ha_launch.h"
+#include "ha_log.h"
 
 namespace ha {
 namespace {
@@ -240,6 +241,8 @@ __global__ __launch_bounds__(NT) void state_scan_fp32_kernel(const float* __rest
 hipError_t launch_state_scan_bf16(const void* ws, const float* alpha, float* state, float* snapshots,
                                   void* sfrag, const Shape& s, hipStream_t st) {
   const int groups = s.B * s.H * (s.d / CWM);
+  HA_LOG("launch state_scan_mfma_kernel<%d>: grid %d x %d threads (%d frames in sequence; snapshots %s)", s.d,
+         groups, (s.d / 32 + 1) * 64, s.F, sfrag ? "as bf16 readout fragments" : snapshots ? "fp32" : "none");
   if (s.d == 128)
     state_scan_mfma_kernel<128><<<groups, (128 / 32 + 1) * 64, 0, st>>>(
         (const unsigned char*)ws, alpha, state, snapshots, (u32x4*)sfrag, s.H, s.F);
@@ -252,6 +255,7 @@ hipError_t launch_state_scan_bf16(const void* ws, const float* alpha, float* sta
 hipError_t launch_state_scan_fp32(const float* gram, const float* alpha, float* state, float* snapshots,
                                   const Shape& s, hipStream_t st) {
   const int groups = s.B * s.H * (s.d / CW);
+  HA_LOG("launch state_scan_fp32_kernel<%d>: grid %d x %d threads (%d frames in sequence)", s.d, groups, NT, s.F);
   if (s.d == 128)
     state_scan_fp32_kernel<128><<<groups, NT, 0, st>>>(gram, alpha, state, snapshots, s.H, s.F);
   else

@@ -24,6 +24,7 @@
 // [8s, 8s + 8) of 32-row block rb are the operand of k-step 2*rb + s.
 #include "ha_device.h"
 #include "ha_launch.h"
+#include "ha_log.h"
 
 namespace ha {
 namespace {
@@ -403,6 +404,7 @@ hipError_t launch_token_level(const void* qp, const void* kp, const void* vp, co
                               hipStream_t st) {
   const int nchf = (s.L + TLC - 1) / TLC;
   const int nchunks = s.B * s.H * s.F * nchf;
+  HA_LOG("launch tl_prep_kernel: grid %d chunks of %d tokens; tl_scan_kernel: grid %d", nchunks, TLC, s.B * s.H * 4);
   tl_prep_kernel<<<nchunks, 256, 0, st>>>((const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vp, alpha, beta,
                                           (unsigned char*)frag, s.H, s.T, s.L, s.F, nchf);
   hipError_t e = hipGetLastError();
