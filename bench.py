@@ -34,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -48,9 +49,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_480p_traffic.txt")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "attn_bf16_480p_clock.txt")
+STATS_FILE = os.path.join(ROOT, "profiles", "layer_{}_kernel_stats.txt")
 PEAK_CLOCK_GHZ = 2.4        # the clock the published peak assumes
 # the attention kernel's sources: the counter summary is valid only for these exact bytes
-ATTN_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("attn_bf16.hip", "ha_device.h")]
+ATTN_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("attn_bf16.hip", "ha_device.h", "ha_dma.h")]
 GATES_SOURCES = [os.path.join(ROOT, "video_dit_hybrid_amd", "csrc", f) for f in ("gates.hip", "ha_device.h", "ha_dma.h")]
 GATES_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gates_480p_traffic.txt")
 
@@ -145,7 +147,7 @@ def cpu_baseline(w, inp, s0, gpu_out, budget_s):
         if time.perf_counter() - t0 - conv > budget_s:
             break
     el = time.perf_counter() - t0 - conv
-    return {"value": done * w.B / el, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done * w.B / el, "unit": "frames/s", "cores": int(threads), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"first {done} of {w.call_frames} frames, all {w.B * w.H} (stream, head) pairs, "
                       f"intra softmax + readout + state update in fp64 numpy; {el:.1f} s"}, worst, done
 
@@ -384,6 +386,17 @@ def attention_roofline(w, t, steps):
             "kernel": "attn_bf16_kernel<128, false> (intra-frame softmax + readout)", "avg_launch_ms": round(ms, 4)}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the baseline line."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def _threads():
     try:
         from threadpoolctl import threadpool_info
@@ -424,7 +437,7 @@ def variant_cpu_baseline(w, inp, mw, gate, s0, budget_s):
         done += 1
         if el > budget_s:
             break
-    return {"value": done * w.B / el, "unit": "frames/s", "cores": int(_threads()), "kind": "oracle",
+    return {"value": done * w.B / el, "unit": "frames/s", "cores": int(_threads()), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"first {done} of {w.frames} frames, all {w.B * w.H} (stream, head) pairs"
                       + (", gate projections from x" if gate is not None else "") +
                       ", per-head maps, intra softmax, readout and state update in fp64 numpy; "
@@ -538,7 +551,7 @@ def bench_kvcache(args):
             if time.perf_counter() - t0 > args.cpu_budget:
                 break
         el = (time.perf_counter() - t0) * H / heads
-        res["cpu_baseline"] = {"value": round(1.0 / el, 4), "unit": f"passes/s at frame {n_cpu}", "cores": int(_threads()),
+        res["cpu_baseline"] = {"value": round(1.0 / el, 4), "unit": f"passes/s at frame {n_cpu}", "cores": int(_threads()), "cpu": cpu_model(),
                                "kind": "oracle", "sample": f"{heads} of {H} heads of one pass of frame {n_cpu} "
                                                            f"({n_cpu + 1} frames of keys) in fp64 numpy, scaled to "
                                                            f"all heads; GPU: {t_kv.get(n_cpu, float('nan')) / P:.3f} ms "
@@ -692,7 +705,7 @@ def bench_token_level(w, args):
             if time.perf_counter() - t0 > args.cpu_budget:
                 break
         el = (time.perf_counter() - t0) * w.H / heads
-        res["cpu_baseline"] = {"value": round(w.B / el, 4), "unit": "frames/s", "cores": int(_threads()),
+        res["cpu_baseline"] = {"value": round(w.B / el, 4), "unit": "frames/s", "cores": int(_threads()), "cpu": cpu_model(),
                                "kind": "oracle", "sample": f"frame 0, {heads} of {w.H} heads (per-token loop in fp64 "
                                                            "numpy, intra softmax), scaled to all heads"}
     print(json.dumps(res), flush=True)
@@ -875,6 +888,15 @@ def main():
     # assumes. Its core-clock cycles per launch (rocprofv3 GRBM_GUI_ACTIVE, a
     # fixed amount of work) over this run's launch time give the clock of this
     # run, and the peak at that clock.
+    # the same launches as a committed kernel-trace summary of this kernel's
+    # sources saw them: the live figure and the kept one side by side
+    if w.name in ("480p", "720p"):
+        kept_us = profile_value(STATS_FILE.format(w.name), "attn_avg_launch_us")
+        if kept_us:
+            roof["profile_summary"] = {"file": os.path.relpath(STATS_FILE.format(w.name), ROOT),
+                                       "avg_launch_ms": round(kept_us / 1e3, 4),
+                                       "frac": round((att + rd) / (kept_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                       "live_over_kept": round(attn_ms / (kept_us / 1e3), 3)}
     cycles = profile_value(CLOCK_FILE, "cycles_per_launch") if w.name == "480p" else None
     if cycles:
         ghz = cycles / (attn_ms * 1e6)
