@@ -89,6 +89,70 @@ def test_edge_frame_lengths(dtype, d, L, F, B, H):
         assert eo < 1e-5 and es < 1e-5
 
 
+# --- one frame per call: the state write as one kernel (d = 128) -------------
+
+@pytest.mark.parametrize("L,B,H,d", [(1560, 1, 12, 128), (1560, 1, 2, 128), (1000, 1, 1, 128), (513, 1, 1, 128),
+                                     (513, 2, 1, 128), (300, 1, 3, 128), (33, 2, 2, 128), (1, 1, 2, 128),
+                                     (520, 1, 2, 64)])
+def test_one_frame_state_write(L, B, H, d):
+    # token splits per (b, h, 32-column block), shape only: (1560, H=12) 6,
+    # (1560, H=2) 6, (1000) 4, (513) 2, the others 1; the last block of a
+    # split may hold 1 to 31 tokens (1560 = 48 x 32 + 24, 1000 = 31 x 32 + 8,
+    # 513 = 16 x 32 + 1); d = 64 takes the gram + scan kernels
+    w = small("480p", B=B, H=H, L=L, d=d, frames=1, state0_sigma=0.05)
+    say(f"case one-frame state write L={L} B={B} H={H} d={d}")
+    eo, es, *_ = full_compare(w, update=True)
+    say(f"  rel_err out {eo:.3e} state {es:.3e}")
+    assert eo < TOL_OUT and es < TOL_STATE
+
+
+def test_one_frame_state_write_snapshot_and_determinism():
+    # the write-only entry point: the snapshot holds S_0 bitwise, and two
+    # calls from the same S_0 give bitwise equal states whichever split of a
+    # column block finishes last
+    w = small("480p", H=12, L=1560, frames=1, state0_sigma=0.05)
+    say("case one-frame state write: snapshot, determinism")
+    inp = W.make_call_inputs(w, 0, 1, 0, clean=True)
+    dev = upload(inp, "bf16")
+    s0 = W.make_state0(w)
+    res = []
+    for _ in range(3):
+        st = torch.from_numpy(s0.copy()).cuda()
+        snap = torch.full((1, w.H, 1, w.d, w.d), float("nan"), device="cuda")
+        api.hybrid_attn_state_update(dev["kp"], dev["vp"], dev["alpha"], dev["beta"], st, w.L, snapshots=snap)
+        torch.cuda.synchronize()
+        res.append((st.cpu().numpy(), snap.cpu().numpy()))
+    assert np.array_equal(res[0][1][0, :, 0], s0[0])
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][0], res[2][0])
+
+
+def test_one_frame_state_write_workspace_reuse():
+    # one workspace for calls on different inputs: a partial sum left by an
+    # earlier call (or garbage in a fresh workspace) must never reach a later
+    # call's sum
+    w = small("480p", H=12, L=1560, frames=1, state0_sigma=0.05)
+    say("case one-frame state write: workspace reuse")
+    s0 = W.make_state0(w)
+    ws = torch.full((api.workspace_bytes(1, w.H, w.L, w.L, w.d, 1),), 0x3F, dtype=torch.uint8, device="cuda")
+    inps = [W.make_call_inputs(w, 0, 1, p, clean=True) for p in (0, 1)]
+    got = []
+    for i in (0, 1, 0):
+        st = torch.from_numpy(s0.copy()).cuda()
+        run_gpu(upload(inps[i], "bf16"), st, w.L, True, workspace=ws)
+        torch.cuda.synchronize()
+        got.append(st.cpu().numpy().astype(np.float64))
+    assert np.array_equal(got[0], got[2])
+    for i, S in ((0, got[0]), (1, got[1])):
+        x = f64(inps[i], "bf16")
+        worst = 0.0
+        for h in range(w.H):
+            S1 = O.delta_update(s0[0, h].astype(np.float64), x["kp"][0, :, h], x["vp"][0, :, h],
+                                float(x["alpha"][0, 0, h]), x["beta"][0, :, h])
+            worst = max(worst, rel_err(S[0, h], S1))
+        say(f"  inputs {i}: rel_err state {worst:.3e} (all heads)")
+        assert worst < TOL_STATE
+
+
 def test_softmax_scale_argument():
     w = small("480p", H=2, L=200, frames=2)
     say("case explicit softmax scale")
@@ -380,12 +444,16 @@ def test_long_stream_constant_memory_and_parity():
     assert worst_s < TOL_STATE and worst_o < TOL_OUT
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("L", [200, 1560])
+def test_graph_replay_matches_eager(L):
     # One frame of a streaming run (a denoise call, then the clean call) captured
     # in a HIP graph and replayed: every replay must equal the eager calls
     # bitwise, with eager work and synchronisations between the replays.
-    w = small("stream", H=2, L=200, frames=1)
-    say("case graph replay")
+    # L = 1560 splits the tokens of the one-frame state write over 6
+    # work-groups per column block (ticket words in the workspace, put back
+    # to 0 by every call).
+    w = small("stream", H=2, L=L, frames=1)
+    say(f"case graph replay L={L}")
     d_in = upload(W.make_call_inputs(w, 0, 1, 0, clean=False), "bf16")
     c_in = upload(W.make_call_inputs(w, 0, 1, w.denoise_passes, clean=True), "bf16")
     s0 = torch.from_numpy(W.make_state0(w)).cuda()

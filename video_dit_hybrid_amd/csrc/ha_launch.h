@@ -121,6 +121,21 @@ inline size_t gram_bytes(const Shape& s) {
   const int n = gram_splits(s);
   return gram_final_bytes(s) * (n > 1 ? 1 + n : 1);
 }
+// One-frame state write in a single kernel (state_step.hip, d = 128, F = 1):
+// S_1 = alpha S_0 + K'^T diag(beta) (V' - K' S_0), the tokens of each (b, h,
+// 32-column block) split over state_step_splits(s) work-groups (shape only)
+// whose sums the last to finish adds up; ws holds state_step_bytes(s) bytes
+// (0 when not split). snapshots, if not null, receives S_0.
+int state_step_splits(const Shape& s);
+size_t state_step_bytes(const Shape& s);
+hipError_t launch_state_step_bf16(const void* kp, const void* vp, const float* alpha, const float* beta,
+                                  float* state, float* snapshots, void* ws, const Shape& s, hipStream_t st);
+// Workspace of the state update: the gram kernels' increments, or what the
+// one-frame kernel needs, whichever is larger (the size query has no dtype).
+inline size_t update_bytes(const Shape& s) {
+  const size_t a = gram_bytes(s), b = state_step_bytes(s);
+  return a > b ? a : b;
+}
 inline size_t snapshot_frag_bytes(const Shape& s) {
   return (size_t)s.B * s.H * s.F * (size_t)s.d * s.d * 2;
 }

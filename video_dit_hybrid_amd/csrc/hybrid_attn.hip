@@ -156,6 +156,9 @@ ha_status run_update(const void* kp, const void* vp, const float* alpha, const f
                      float* state, float* snaps, float* gram, const ha::Shape& s, int dtype,
                      hipStream_t st, void* sfrag = nullptr) {
   if (dtype == HA_BF16) {
+    // one frame, d = 128: the residual, the increment and the decay in one kernel
+    if (s.F == 1 && s.d == 128 && !sfrag)
+      return launched(ha::launch_state_step_bf16(kp, vp, alpha, beta, state, snaps, gram, s, st));
     if (ha::launch_gram_bf16(kp, vp, beta, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
     return launched(ha::launch_state_scan_bf16(gram, alpha, state, snaps, sfrag, s, st));
   }
@@ -204,6 +207,15 @@ bool workspace_overlaps(const ForwardArgs& a, const ha::Shape& s, const void* ws
   return written_overlaps({{a.out, tb}}, {{a.q, tb}, {a.k, tb}, {a.v, tb}, {a.qp, tb}, {a.state, stb}});
 }
 
+// Workspace of a forward call: the state update's increments and, over
+// several frames, the per-frame states.
+size_t forward_base_bytes(const ha::Shape& s, int update_state) {
+  if (!update_state) return 0;
+  size_t n = align_up(ha::update_bytes(s));
+  if (s.F > 1) n += align_up(ha::snapshot_bytes(s));
+  return n;
+}
+
 // Launch order of a validated forward call (see the top of this file).
 ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspace, hipStream_t st) {
   const float scale = resolve_scale(a.softmax_scale, a.d);
@@ -217,7 +229,7 @@ ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspa
     r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st);
     return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
   }
-  void* snap_area = (char*)workspace + align_up(ha::gram_bytes(s));
+  void* snap_area = (char*)workspace + align_up(ha::update_bytes(s));
   if (a.dtype == HA_BF16) {
     // S_{n-1} of every frame as bf16 readout fragments (the readout rounds the
     // state to bf16 either way)
@@ -259,16 +271,13 @@ const char* hybrid_attn_status_string(ha_status status) {
 size_t hybrid_attn_state_workspace_bytes(int B, int H, int T, int frame_len, int d) {
   ha::Shape s;
   if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK) return 0;
-  return align_up(ha::gram_bytes(s));
+  return align_up(ha::update_bytes(s));
 }
 
 size_t hybrid_attn_workspace_bytes(int B, int H, int T, int frame_len, int d, int update_state) {
   ha::Shape s;
-  if (!update_state) return 0;
   if (check_shape(B, H, T, d, frame_len, HA_BF16, &s) != HA_OK) return 0;
-  size_t n = align_up(ha::gram_bytes(s));
-  if (s.F > 1) n += align_up(ha::snapshot_bytes(s));
-  return n;
+  return forward_base_bytes(s, update_state);
 }
 
 ha_status hybrid_attn_intra_readout(const void* q, const void* k, const void* v, const void* qp,
