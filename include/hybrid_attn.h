@@ -90,8 +90,14 @@ typedef enum HA_ENUM_INT {
  * pre-update states S_{N-1} (d x d fp32 each). A call with fewer than 128
  * (stream, head, frame) groups computes each frame's increments in
  * n = min(ceil(256 / groups), 16, ceil(frame_len / 64)) token splits and needs n
- * more d x 2d fp32 blocks per group for their partial sums. The size depends on
- * the arguments only. Returns 0 for invalid sizes.
+ * more d x 2d fp32 blocks per group for their partial sums. A bf16 call with
+ * one frame and d = 128 writes the state in one kernel instead, whose u =
+ * B * H * 4 (stream, head, 32-column) units split their tokens over
+ * m = min(floor(256 / u), floor(ceil(frame_len / 32) / 8), 16) work-groups and,
+ * when m > 1, need u * m * 16 KiB of partial sums plus 8 bytes per unit (each
+ * rounded up to 256 bytes); the size returned is the larger of the two (the
+ * query has no dtype). The size depends on the arguments only. Returns 0 for
+ * invalid sizes.
  */
 size_t hybrid_attn_workspace_bytes(int B, int H, int T, int frame_len, int d,
                                    int update_state);

@@ -29,6 +29,16 @@ def test_library_exports_every_declared_symbol():
     assert set(api.EXPORTS) == set(names)
 
 
+def test_debug_library_exports_every_declared_symbol():
+    # the build with device index checks (__graft_entry__.build() makes both)
+    from video_dit_hybrid_amd import build as B
+    if not os.path.exists(B.DEBUG_LIB_PATH):
+        pytest.skip("the debug library is not built")
+    L = ctypes.CDLL(B.DEBUG_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
 def test_version_and_status_strings():
     assert api.lib().hybrid_attn_version() >= 100
     for code in range(10):

@@ -23,7 +23,11 @@ EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_in
            "hybrid_attn_forward_token_level", "hybrid_attn_token_level_workspace_bytes",
            "hybrid_attn_forward_noalloc", "hybrid_attn_noalloc_scratch_bytes")
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybrid_attn.so")
+_PKG = os.path.dirname(os.path.abspath(__file__))
+# HYBRID_ATTN_LIBRARY=debug selects the build with device index checks
+# (libhybrid_attn_debug.so, built beside the release library)
+LIB_PATH = os.path.join(_PKG, "libhybrid_attn_debug.so" if os.environ.get("HYBRID_ATTN_LIBRARY") == "debug"
+                        else "libhybrid_attn.so")
 _lib = None
 
 

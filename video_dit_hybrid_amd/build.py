@@ -48,14 +48,23 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+DEBUG_BUILD = os.path.join(BUILD, "debug")
+DEBUG_LIB_PATH = os.path.join(PKG, "libhybrid_attn_debug.so")
+
+
+def build(verbose: bool = False, extra_flags=(), debug: bool = False) -> str:
+    """Compile every HIP source and link the shared library; returns its path.
+    debug: the same sources with -DHA_DEBUG (device index checks, reported by
+    every entry point after synchronising its stream) into
+    libhybrid_attn_debug.so beside the release library."""
+    bdir, lib_path = (DEBUG_BUILD, DEBUG_LIB_PATH) if debug else (BUILD, LIB_PATH)
+    extra_flags = (*extra_flags, "-DHA_DEBUG") if debug else tuple(extra_flags)
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         cmd = [cc, *HIP_FLAGS, *extra_flags, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
         out = _run(cmd)
         if verbose and out.strip():
@@ -64,12 +73,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print("built", LIB_PATH)
-    return LIB_PATH
+        print("built", lib_path)
+    return lib_path
 
 
 SANITIZE_DIR = os.path.join(BUILD, "host_sanitized")
@@ -111,4 +120,4 @@ if __name__ == "__main__":
     if "--host-sanitized" in sys.argv:
         build_host_sanitized(verbose=True)
     else:
-        build(verbose="-v" in sys.argv)
+        build(verbose="-v" in sys.argv, debug="--debug" in sys.argv)

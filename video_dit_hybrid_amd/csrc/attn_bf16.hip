@@ -156,6 +156,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int lr = lane & 31, hh = lane >> 5;
+  // debug bit 1: the work item decodes to a valid (b, h, frame, query tile, split)
+  HA_CHECK(qt >= 0 && qt < qtiles && h >= 0 && h < H && n >= 0 && n < F && b >= 0 && sp >= 0 && sp < nsplit, 1);
   const uint32_t rsb = (uint32_t)H * D * 2;  // bytes between consecutive tokens
   const long long fbase = ((long long)b * T + (long long)n * L) * ((long long)H * D) + (long long)h * D;
   // bytes of this (b, h, frame) slab as one buffer: tokens >= L read as zero
@@ -251,6 +253,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
 
   const int ntiles = (nkeys + KT - 1) / KT;
   const int last_valid = nkeys - (ntiles - 1) * KT;  // keys in the last tile
+  // debug bit 2: a non-empty key range; bit 4: the last LDS operand reads of a
+  // tile (K rows through ds_read_b128, V^T through transposed reads) stay
+  // inside the tile
+  HA_CHECK(nkeys > 0 && t0 >= 0 && last_valid >= 1 && last_valid <= KT, 2);
+  HA_CHECK((kaddr ^ ((C::KSTEPS - 1) << 5)) + 32 * D * 2 + 16 <= C::TILE &&
+               v_off(32 + 16 + 4, C::DB - 1) + 8 <= C::TILE,
+           4);
 
   // S^T for one tile (two 32-key blocks) from K buffer kb_. MFMA i uses the K
   // operand (ks, kb) = (i/2, i%2); operands are read PF MFMAs ahead.
@@ -370,6 +379,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
                   float& mt_n) {
     using Fl = decltype(flags);
     constexpr int P = Fl::P;
+    // debug bit 2: the tiles this step copies exist
+    HA_CHECK((!Fl::LOADK || j + 2 < ntiles) && (!Fl::NEXT || j + 1 < ntiles), 2);
     if constexpr (Fl::LOADK) issue_k(j + 2, P);
     else if (j + 2 < ntiles) issue_k(j + 2, P);
     if constexpr (Fl::NEXT) issue_v(j + 1, P ^ 1);
@@ -658,6 +669,8 @@ hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v
                                                                         (uint16_t*)out, rows, nsplit);
   return hipGetLastError();
 }
+
+HA_DEBUG_READER(debug_take_attn)
 
 hipError_t launch_kv_append(const void* k, const void* v, void* k_cache, void* v_cache, int cache_tokens,
                             int at_token, const Shape& s, hipStream_t st) {

@@ -131,4 +131,29 @@ __device__ __forceinline__ int xcd_major_item(int n_groups) {
   return (g & 7) * per_xcd + (g >> 3);
 }
 
+// Index checks of the debug build (compiled with -DHA_DEBUG; empty otherwise).
+// A failed check ORs its bit into this translation unit's debug word with a
+// vector atomic and the kernel goes on (no trap); the entry point reads and
+// clears the words after its launches and reports the bits. Each kernel file
+// defines its reader with HA_DEBUG_READER.
+#if defined(HA_DEBUG)
+static __device__ unsigned int g_debug_word;
+#define HA_CHECK(cond, bit)                                                       \
+  do {                                                                            \
+    if (!(cond)) atomicOr(&::ha::g_debug_word, (unsigned)(bit));                  \
+  } while (0)
+#define HA_DEBUG_READER(fn)                                                       \
+  unsigned fn() {                                                                 \
+    unsigned v = 0, z = 0;                                                        \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(::ha::g_debug_word), sizeof v) != hipSuccess) return ~0u; \
+    if (hipMemcpyToSymbol(HIP_SYMBOL(::ha::g_debug_word), &z, sizeof z) != hipSuccess) return ~0u;   \
+    return v;                                                                     \
+  }
+#else
+#define HA_CHECK(cond, bit) \
+  do {                      \
+  } while (0)
+#define HA_DEBUG_READER(fn)
+#endif
+
 }  // namespace ha

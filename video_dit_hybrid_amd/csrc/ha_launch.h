@@ -143,4 +143,13 @@ inline size_t snapshot_bytes(const Shape& s) {
   return (size_t)s.B * s.H * s.F * (size_t)s.d * s.d * sizeof(float);
 }
 
+#if defined(HA_DEBUG)
+// Debug words of the kernel files (bit set = an index check failed), read and
+// cleared: attention, gram (state increments), scan, one-frame state write.
+unsigned debug_take_attn();
+unsigned debug_take_gram();
+unsigned debug_take_scan();
+unsigned debug_take_step();
+#endif
+
 }  // namespace ha

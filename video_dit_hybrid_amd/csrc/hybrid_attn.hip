@@ -246,6 +246,33 @@ ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspa
   return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
 }
 
+// Debug build (-DHA_DEBUG): after an entry point's launches, wait for them and
+// report every failed index check of the kernels (the kernel files' debug
+// words) on stderr, as HA_ERR_DEVICE. Other builds return r as it is.
+ha_status debug_finish(const char* entry, ha_status r, hipStream_t st) {
+#if defined(HA_DEBUG)
+  if (r != HA_OK) return r;
+  if (hipStreamSynchronize(st) != hipSuccess) return HA_ERR_DEVICE;
+  const struct {
+    const char* name;
+    unsigned (*take)();
+  } files[] = {{"attention", ha::debug_take_attn}, {"gram", ha::debug_take_gram},
+               {"state scan", ha::debug_take_scan}, {"one-frame state write", ha::debug_take_step}};
+  for (const auto& f : files) {
+    const unsigned w = f.take();
+    if (w) {
+      fprintf(stderr, "[hybrid_attn debug] %s: index check bits 0x%x failed in the %s kernel\n", entry, w, f.name);
+      r = HA_ERR_DEVICE;
+    }
+  }
+  return r;
+#else
+  (void)entry;
+  (void)st;
+  return r;
+#endif
+}
+
 }  // namespace
 
 extern "C" {
@@ -301,8 +328,9 @@ ha_status hybrid_attn_intra_readout(const void* q, const void* k, const void* v,
       overlap(out, tb, qp, tb) || overlap(out, tb, states, sb))
     return HA_ERR_ALIAS;
   log_call("hybrid_attn_intra_readout", s, dtype, 0, 0);
-  return run_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame, out, s, dtype,
-                     resolve_scale(softmax_scale, d), (hipStream_t)stream);
+  return debug_finish("hybrid_attn_intra_readout",
+                      run_readout(q, k, v, qp, states, state_stride_bh, state_stride_frame, out, s, dtype,
+                     resolve_scale(softmax_scale, d), (hipStream_t)stream), (hipStream_t)stream);
 }
 
 ha_status hybrid_attn_state_update(const void* kp, const void* vp, const float* alpha,
@@ -327,7 +355,8 @@ ha_status hybrid_attn_state_update(const void* kp, const void* vp, const float* 
     return HA_ERR_ALIAS;
   log_call("hybrid_attn_state_update", s, dtype, 1, need);
   r = run_update(kp, vp, alpha, beta, state, snapshots, (float*)workspace, s, dtype, (hipStream_t)stream);
-  return r != HA_OK ? r : check_finite("state", state, stb / sizeof(float), (hipStream_t)stream);
+  if (r == HA_OK) r = check_finite("state", state, stb / sizeof(float), (hipStream_t)stream);
+  return debug_finish("hybrid_attn_state_update", r, (hipStream_t)stream);
 }
 
 ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const void* qp,
@@ -346,7 +375,8 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
   if (need > 0 && (!workspace || workspace_bytes < need)) return HA_ERR_WORKSPACE;
   if (workspace_overlaps(a, s, workspace, need)) return HA_ERR_ALIAS;
   log_call("hybrid_attn_forward", s, dtype, update_state, need);
-  return launch_forward(a, s, workspace, (hipStream_t)stream);
+  return debug_finish("hybrid_attn_forward",
+                      launch_forward(a, s, workspace, (hipStream_t)stream), (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -472,8 +502,9 @@ ha_status hybrid_attn_forward_fmap(const void* q, const void* k, const void* v, 
                                       {{q, tb}, {k, tb}, {v, tb}, {wq, wb}, {state, stb}}))
     return HA_ERR_ALIAS;
   log_call("hybrid_attn_forward_fmap", s, dtype, update_state, lay.total);
-  return fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, (char*)workspace, lay, s, update_state,
-                  resolve_scale(softmax_scale, d), (hipStream_t)stream);
+  r = fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, (char*)workspace, lay, s, update_state,
+               resolve_scale(softmax_scale, d), (hipStream_t)stream);
+  return debug_finish("hybrid_attn_forward_fmap", r, (hipStream_t)stream);
 }
 
 size_t hybrid_attn_gated_workspace_bytes(int B, int H, int T, int frame_len, int d, int update_state) {
@@ -522,17 +553,21 @@ ha_status hybrid_attn_forward_gated(const void* x, const void* q, const void* k,
   const float scale = resolve_scale(softmax_scale, d);
   log_call("hybrid_attn_forward_gated", s, dtype, update_state, lay.total);
   if (!update_state)
-    return fmap_run(q, k, v, wq, wk, wv, nullptr, nullptr, nullptr, state, out, ws, lay, s, 0, scale, st);
+    return debug_finish("hybrid_attn_forward_gated",
+                        fmap_run(q, k, v, wq, wk, wv, nullptr, nullptr, nullptr, state, out, ws, lay, s, 0, scale, st),
+                        st);
   float* alpha = (float*)(ws + lay.alpha);
   float* beta = (float*)(ws + lay.beta);
   if (ha::launch_gates(x, w_gate, b_gate, alpha, beta, (float*)(ws + lay.apart), C, s, st) != hipSuccess)
     return HA_ERR_DEVICE;
   if (!normalize_k)
-    return fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, ws, lay, s, 1, scale, st);
+    return debug_finish("hybrid_attn_forward_gated",
+                        fmap_run(q, k, v, wq, wk, wv, alpha, beta, nullptr, state, out, ws, lay, s, 1, scale, st), st);
   float* bgv = (float*)(ws + lay.beta_g);
   float* bbv = (float*)(ws + lay.beta_b);
   if (ha::launch_keyscale(k, wk, beta, bgv, bbv, s, st) != hipSuccess) return HA_ERR_DEVICE;
-  return fmap_run(q, k, v, wq, wk, wv, alpha, bgv, bbv, state, out, ws, lay, s, 1, scale, st);
+  return debug_finish("hybrid_attn_forward_gated",
+                      fmap_run(q, k, v, wq, wk, wv, alpha, bgv, bbv, state, out, ws, lay, s, 1, scale, st), st);
 }
 
 size_t hybrid_attn_gates_workspace_bytes(int B, int H, int T, int frame_len) {
@@ -563,7 +598,9 @@ ha_status hybrid_attn_gates(const void* x, const void* w_gate, const float* b_ga
       overlap(beta, bb, b_gate, (size_t)2 * H * 4))
     return HA_ERR_ALIAS;
   log_call("hybrid_attn_gates", s, dtype, 0, wsb);
-  return launched(ha::launch_gates(x, w_gate, b_gate, alpha, beta, (float*)workspace, C, s, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  return debug_finish("hybrid_attn_gates",
+                      launched(ha::launch_gates(x, w_gate, b_gate, alpha, beta, (float*)workspace, C, s, st)), st);
 }
 
 }  // extern "C"
@@ -628,9 +665,11 @@ ha_status hybrid_attn_kvcache_forward(const void* q, const void* k, const void* 
   if (ha::launch_kv_append(k, v, k_cache, v_cache, cap, frame_index * frame_len, s, st) != hipSuccess)
     return HA_ERR_DEVICE;
   char* ws = (char*)workspace;
-  return launched(ha::launch_attn_kv_bf16(q, k_cache, v_cache, out, lay.total ? (float*)(ws + lay.part_o) : nullptr,
-                                          lay.total ? (void*)(ws + lay.part_ml) : nullptr, lay.nsplit, cap,
-                                          frame_index * frame_len, s, resolve_scale(softmax_scale, d), st));
+  const ha_status r2 = launched(ha::launch_attn_kv_bf16(
+      q, k_cache, v_cache, out, lay.total ? (float*)(ws + lay.part_o) : nullptr,
+      lay.total ? (void*)(ws + lay.part_ml) : nullptr, lay.nsplit, cap, frame_index * frame_len, s,
+      resolve_scale(softmax_scale, d), st));
+  return debug_finish("hybrid_attn_kvcache_forward", r2, st);
 }
 
 }  // extern "C"
@@ -691,7 +730,8 @@ ha_status hybrid_attn_forward_token_level(const void* q, const void* k, const vo
     return HA_ERR_DEVICE;
   r = launched(ha::launch_attn_kv_bf16(q, k, v, out, nullptr, nullptr, 1, T, -1, s, resolve_scale(softmax_scale, d),
                                        st, oint));
-  return r != HA_OK || !update_state ? r : check_finite("state", state, stb / sizeof(float), st);
+  return debug_finish("hybrid_attn_forward_token_level",
+                      r != HA_OK || !update_state ? r : check_finite("state", state, stb / sizeof(float), st), st);
 }
 
 }  // extern "C"
@@ -748,7 +788,8 @@ ha_status hybrid_attn_forward_noalloc(const void* q, const void* k, const void* 
   if (need > 0 && (r = scratch_of_current_device(&ws)) != HA_OK) return r;
   if (workspace_overlaps(a, s, ws, need)) return HA_ERR_ALIAS;
   log_call("hybrid_attn_forward_noalloc", s, dtype, update_state, need);
-  return launch_forward(a, s, ws, (hipStream_t)stream);
+  return debug_finish("hybrid_attn_forward_noalloc",
+                      launch_forward(a, s, ws, (hipStream_t)stream), (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -137,6 +137,12 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   const int nch_all = (L + TC - 1) / TC;
   const int c0 = (int)((long long)sp * nch_all / nsplit);
   const int nch = (int)((long long)(sp + 1) * nch_all / nsplit) - c0;
+  // debug bit 1: a valid (b, h, frame, split) and chunk range; bit 2: the last
+  // transposed operand read of a chunk stays inside its tile
+  HA_CHECK(h >= 0 && h < H && n >= 0 && n < F && b >= 0 && sp < nsplit && c0 >= 0 && nch >= 0 &&
+               c0 + nch <= nch_all,
+           1);
+  HA_CHECK(tr_off(16 * (KSC - 1) + 4, NRB - 1) + 8 <= TILE, 2);
   for (int c = 0; c < NBUF - 1 && c < nch; ++c) issue(c0 + c, c);
   for (int c = 0; c < nch; ++c) {
     const int buf = c % NBUF;
@@ -296,6 +302,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 }
 
 }  // namespace
+
+HA_DEBUG_READER(debug_take_gram)
 
 hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float* beta, const float* beta2,
                                      float* partial, int nsplit, const Shape& s, hipStream_t st) {

@@ -57,6 +57,9 @@ __global__ __launch_bounds__((D / 32 + 1) * 64) void state_scan_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
+  // debug bit 1: one work-group per (b, h, column block), a loader wave past
+  // the compute waves
+  HA_CHECK(cb >= 0 && cb < NCB && h >= 0 && h < H && b >= 0 && wave <= NRB, 1);
 
   if (wave == NRB) {
     // ---- loader: -G_n of frame n into gbuf[n % 2], lane-linear (fragment order kept)
@@ -142,6 +145,7 @@ __global__ __launch_bounds__((D / 32 + 1) * 64) void state_scan_mfma_kernel(
 
   auto step = [&](auto slot_c, int n) {
     constexpr int SL = decltype(slot_c)::value;
+    HA_CHECK(n >= 0 && n < F && (n & 1) == SL, 2);  // debug bit 2: frame n in buffer n % 2
     lds_barrier();  // E_n
     u32x4 gh[KS], gl[KS];
     const u32x4* gp = reinterpret_cast<const u32x4*>(&gbuf[SL][0]);
@@ -237,6 +241,8 @@ __global__ __launch_bounds__(NT) void state_scan_fp32_kernel(const float* __rest
 }
 
 }  // namespace
+
+HA_DEBUG_READER(debug_take_scan)
 
 hipError_t launch_state_scan_bf16(const void* ws, const float* alpha, float* state, float* snapshots,
                                   void* sfrag, const Shape& s, hipStream_t st) {

@@ -123,6 +123,7 @@ __global__ __launch_bounds__(SW * 64, 1) void state_step_kernel(
   // 64-byte rows) and beta -> this wave's LDS slot
   auto issue = [&](int m, int slot) {
     const int kb = k0 + wave + SW * m;
+    HA_CHECK(kb >= k0 && kb < k1 && slot >= 0 && slot < NSLOT, 2);  // debug bit 2: a block of this split
     const uint32_t base = lds0 + (wave * NSLOT + slot) * BUF;
     const uint32_t toff = (uint32_t)kb * TB * rsb;
 #pragma unroll
@@ -166,10 +167,14 @@ __global__ __launch_bounds__(SW * 64, 1) void state_step_kernel(
   // transposed reads of K'^T (group g = lane / 16 reads rows base + gi / 4,
   // columns 32 rb + 16 (g % 2) + 4 (gi % 4))
   const int ka = j * (SD * 2) + ((hh ^ swz(j)) << 4);
+  // debug bit 1: a valid unit and split, block range inside the frame; bit 4:
+  // the last row and transposed reads of a block stay inside its K' tile
+  HA_CHECK(cb < NCB && h < H && b >= 0 && sp < nsplit && k0 >= 0 && k0 <= k1 && k1 <= nblk, 1);
   auto tr_off = [&](int row, int rb) {
     const int col = 32 * rb + 16 * (g & 1) + 4 * (gi & 3);
     return row * (SD * 2) + (((col >> 3) ^ swz(row)) << 4) + (col & 7) * 2;
   };
+  HA_CHECK((ka ^ ((KS - 1) << 5)) + 16 <= KBLK && tr_off(TB - 1, NRB - 1) + 8 <= KBLK, 4);
 
   // the S_0 elements this thread writes S_1 of at the end (rows 32 wave +
   // 8 v4 + 4 hh + e of column 32 cb + j), loaded now so that their latency
@@ -371,6 +376,8 @@ unsigned long long next_tag() {
 size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 }  // namespace
+
+HA_DEBUG_READER(debug_take_step)
 
 int state_step_splits(const Shape& s) {
   // one work-group per CU (the kernel holds -S_0 and the increment in
