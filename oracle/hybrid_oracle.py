@@ -52,6 +52,9 @@ per-token gated delta rule) is here as hybrid_layer_token_level: every token
 reads the state left by all earlier tokens, and every token of a clean pass
 writes it; the frame's forget gate applies once, at its first token.
 
+A per-branch output weight (hybrid_layer_mixed) covers the mixtures of
+softmax and linear branches that the LinVideo and SALAD pages describe.
+
 Every function here is pinned by tests/test_oracle_pins.py against
 properties the page and the mathematics fix (row sums, closed forms, the
 delta-rule recall property, brute force on tiny inputs, textbook attention).
@@ -146,6 +149,39 @@ def hybrid_layer(q, k, v, qp, kp, vp, alpha, beta, state, frame_len,
             out[b, :, h], st[b, h] = hybrid_layer_head(
                 q[b, :, h], k[b, :, h], v[b, :, h], qp[b, :, h], kk, vv, a, bt,
                 st[b, h], frame_len, update_state, scale)
+    return out, st
+
+
+def hybrid_layer_mixed(q, k, v, qp, kp, vp, alpha, beta, state, frame_len,
+                       update_state, mix, scale=None):
+    """The layer with a weight on each branch's output:
+        O = w_softmax * O_intra + w_inter * O_inter,
+    mix [B, H, 2] = (w_softmax, w_inter) per (stream, head), the same for every
+    frame of the call. This covers the mixtures the pages describe for
+    swapping softmax layers to linear ones: LinVideo's selective transfer,
+    o = r SoftmaxAttn + (1 - r) LinearAttn with a learned r in [0, 1] per
+    layer (weights (r, 1 - r)), and SALAD's input- and timestep-dependent
+    scale s in (0, 1) on the linear branch (weights (1, s)). The weights touch
+    the output only; the state recursion is that of hybrid_layer.
+    Returns (out [B, T, H, d_v], state_out).
+    """
+    B, T, H, _ = q.shape
+    L = int(frame_len)
+    F = T // L
+    out = np.empty((B, T, H, v.shape[3]), dtype=np.float64)
+    st = np.array(state, dtype=np.float64, copy=True)
+    for b in range(B):
+        for h in range(H):
+            w_soft, w_inter = float(mix[b, h, 0]), float(mix[b, h, 1])
+            S = st[b, h]
+            for n in range(F):
+                r = slice(n * L, (n + 1) * L)
+                o_intra = intra_frame_attention(q[b, r, h], k[b, r, h], v[b, r, h], scale)
+                o_inter = inter_frame_readout(qp[b, r, h], S)
+                out[b, r, h] = w_soft * o_intra + w_inter * o_inter
+                if update_state:
+                    S = delta_update(S, kp[b, r, h], vp[b, r, h], float(alpha[b, n, h]), beta[b, r, h])
+            st[b, h] = S
     return out, st
 
 

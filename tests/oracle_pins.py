@@ -692,7 +692,75 @@ def check_token_level_denoise_and_causality(o):
     assert np.array_equal(out2[:6], out[:6]) and not np.allclose(out2[6], out[6])
 
 
+def _mix_inputs(rng, B=2, H=3, d=4, L=4, F=3):
+    q, k, v, qp, kp, vp, a, b, s = _inputs(rng, B, F * L, H, d, L)
+    mix = rng.uniform(-1.0, 2.0, size=(B, H, 2))
+    return q, k, v, qp, kp, vp, a, b, s, mix, L
+
+
+def check_mix_unit_weights_is_the_plain_layer(o):
+    """Weights (1, 1) give the plain sum O_intra + O_inter exactly, and the
+    state never depends on the weights."""
+    rng = np.random.default_rng(41)
+    q, k, v, qp, kp, vp, a, b, s, mix, L = _mix_inputs(rng)
+    ref, Sref = o.hybrid_layer(q, k, v, qp, kp, vp, a, b, s, L, 1)
+    out, S = o.hybrid_layer_mixed(q, k, v, qp, kp, vp, a, b, s, L, 1, np.ones_like(mix))
+    assert np.array_equal(out, ref) and np.array_equal(S, Sref)
+    _, S2 = o.hybrid_layer_mixed(q, k, v, qp, kp, vp, a, b, s, L, 1, mix)
+    assert np.array_equal(S2, Sref)
+
+
+def check_mix_softmax_only_is_textbook_attention(o):
+    """LinVideo r = 1 (weights (1, 0)): every frame is plain per-frame softmax
+    attention whatever the state; r = 0 (weights (0, 1)): Q'_N S_{N-1} by scalar
+    loops over a state chain computed token by token."""
+    import torch
+    rng = np.random.default_rng(42)
+    q, k, v, qp, kp, vp, a, b, s, mix, L = _mix_inputs(rng, B=1, H=2, d=3, L=3, F=2)
+    B, T, H, d = q.shape
+    out, _ = o.hybrid_layer_mixed(q, k, v, qp, kp, vp, a, b, s, L, 1, np.tile([1.0, 0.0], (B, H, 1)))
+    for n in range(T // L):
+        r = slice(n * L, (n + 1) * L)
+        tq, tk, tv = (torch.from_numpy(x[:, r]).permute(0, 2, 1, 3) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).permute(0, 2, 1, 3).numpy()
+        assert np.max(np.abs(out[:, r] - ref)) < 1e-12
+    out, _ = o.hybrid_layer_mixed(q, k, v, qp, kp, vp, a, b, s, L, 1, np.tile([0.0, 1.0], (B, H, 1)))
+    for h in range(H):
+        S = [[float(s[0, h, i, j]) for j in range(d)] for i in range(d)]
+        for n in range(T // L):
+            for t in range(n * L, (n + 1) * L):
+                for j in range(d):
+                    want = sum(qp[0, t, h, i] * S[i][j] for i in range(d))
+                    assert abs(out[0, t, h, j] - want) < 1e-12
+            an = float(a[0, n, h])
+            new = [[an * S[i][j] for j in range(d)] for i in range(d)]
+            for t in range(n * L, (n + 1) * L):
+                resid = [vp[0, t, h, j] - sum(kp[0, t, h, i] * S[i][j] for i in range(d)) for j in range(d)]
+                for i in range(d):
+                    for j in range(d):
+                        new[i][j] += kp[0, t, h, i] * float(b[0, t, h]) * resid[j]
+            S = new
+
+
+def check_mix_weights_per_stream_and_head(o):
+    """Each (stream, head) takes its own pair: the output is linear in the two
+    weights, with the branches of weights (1, 0) and (0, 1)."""
+    rng = np.random.default_rng(43)
+    q, k, v, qp, kp, vp, a, b, s, mix, L = _mix_inputs(rng, B=2, H=3)
+    B, _, H, _ = q.shape
+    o10, _ = o.hybrid_layer_mixed(q, k, v, qp, kp, vp, a, b, s, L, 1, np.tile([1.0, 0.0], (B, H, 1)))
+    o01, _ = o.hybrid_layer_mixed(q, k, v, qp, kp, vp, a, b, s, L, 1, np.tile([0.0, 1.0], (B, H, 1)))
+    out, _ = o.hybrid_layer_mixed(q, k, v, qp, kp, vp, a, b, s, L, 1, mix)
+    for bb in range(B):
+        for h in range(H):
+            want = mix[bb, h, 0] * o10[bb, :, h] + mix[bb, h, 1] * o01[bb, :, h]
+            assert np.max(np.abs(out[bb, :, h] - want)) < 1e-12
+
+
 ALL_CHECKS = [
+    check_mix_unit_weights_is_the_plain_layer,
+    check_mix_softmax_only_is_textbook_attention,
+    check_mix_weights_per_stream_and_head,
     check_token_level_one_token_frames,
     check_token_level_beta0_closed_form,
     check_token_level_brute_force_and_recall,

@@ -230,7 +230,26 @@ def _token_variant(m, decay_every_token=False, read_after=False, decayed_residua
     m.hybrid_layer_token_level = f
 
 
+def _mix_variant(m, swap=False, transpose=False, scale_update=False):
+    base = m.hybrid_layer_mixed
+
+    def f(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, mix, scale=None):
+        mx = np.array(mix, dtype=np.float64, copy=True)
+        if swap:
+            mx = mx[:, :, ::-1]
+        if transpose:  # an off-by-one head index: head h takes head h - 1's pair
+            mx = np.roll(mx, 1, axis=1)
+        out, st = base(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, mx, scale)
+        if scale_update and update_state:
+            st = st * mx[:, :, 1][:, :, None, None]
+        return out, st
+    m.hybrid_layer_mixed = f
+
+
 MUTANTS = {
+    "mix_weights_swapped": lambda m: _mix_variant(m, swap=True),
+    "mix_head_index_shifted": lambda m: _mix_variant(m, transpose=True),
+    "mix_scales_the_state": lambda m: _mix_variant(m, scale_update=True),
     "token_decay_every_token": lambda m: _token_variant(m, decay_every_token=True),
     "token_reads_own_write": lambda m: _token_variant(m, read_after=True),
     "token_decayed_residual": lambda m: _token_variant(m, decayed_residual=True),
