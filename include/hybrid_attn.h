@@ -129,6 +129,30 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v,
                               float softmax_scale, void* stream);
 
 /*
+ * hybrid_attn_forward with a weight on each branch's output: for stream b and
+ * head h, O = w_softmax O_intra + w_inter O_inter with (w_softmax, w_inter) =
+ * (mix[2 (b H + h)], mix[2 (b H + h) + 1]) for every frame of the call. The
+ * pages' mixtures of a softmax and a linear branch are such pairs: LinVideo's
+ * selective transfer ("LinVideo" page: o = r SoftmaxAttn + (1 - r) LinearAttn,
+ * a learned r in [0, 1] per layer) is (r, 1 - r); SALAD's input- and
+ * timestep-aware scale on the linear branch ("SALAD" page, ITADS: s in (0, 1)
+ * through a sigmoid) is (1, s). The weights touch the output only; the state
+ * update is that of hybrid_attn_forward.
+ *   mix   fp32 [B, H, 2], device memory, 8-byte aligned; required (NULL gives
+ *         HA_ERR_NULL). Read only.
+ * Other arguments, workspace and errors as hybrid_attn_forward; bf16 only
+ * (HA_ERR_UNSUPPORTED for fp32); HA_ERR_ALIAS also when out overlaps mix.
+ */
+ha_status hybrid_attn_forward_mix(const void* q, const void* k, const void* v,
+                                  const void* qp, const void* kp, const void* vp,
+                                  const float* alpha, const float* beta,
+                                  float* state, void* out, const float* mix,
+                                  void* workspace, size_t workspace_bytes,
+                                  int B, int H, int T, int d, int frame_len,
+                                  ha_dtype dtype, int update_state,
+                                  float softmax_scale, void* stream);
+
+/*
  * hybrid_attn_forward for callers that cannot allocate: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. Arguments,
  * results and errors are those of hybrid_attn_forward without the workspace:

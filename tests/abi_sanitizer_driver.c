@@ -123,6 +123,16 @@ int main(void) {
   expect("forward alias ws/q", FWD(buf(0), buf(8), buf(9), buf(0), ws, T, L, d, 1), HA_ERR_ALIAS);
   expect("forward alias out/state", FWD(buf(0), buf(8), buf(8), buf(10), ws, T, L, d, 1), HA_ERR_ALIAS);
 #undef FWD
+#define MIXF(mix_, out_, dt_)                                                                                  \
+  hybrid_attn_forward_mix(P(buf(0)), P(buf(1)), P(buf(2)), P(buf(3)), P(buf(4)), P(buf(5)),                     \
+                          (const float*)P(buf(6)), (const float*)P(buf(7)), (float*)P(buf(8)), P(out_),         \
+                          (const float*)P(mix_), P(buf(10)), ws, B, H, T, d, L, dt_, 1, 0.0f, NULL)
+  expect("mix valid (no device)", MIXF(buf(11), buf(9), HA_BF16), HA_ERR_DEVICE);
+  expect("mix null weights", MIXF(0, buf(9), HA_BF16), HA_ERR_NULL);
+  expect("mix misaligned weights", MIXF(buf(11) + 4, buf(9), HA_BF16), HA_ERR_ALIGN);
+  expect("mix fp32", MIXF(buf(11), buf(9), HA_FP32), HA_ERR_UNSUPPORTED);
+  expect("mix alias out/weights", MIXF(buf(11), buf(11), HA_BF16), HA_ERR_ALIAS);
+#undef MIXF
   expect("noalloc too large",
          hybrid_attn_forward_noalloc(P(buf(0)), P(buf(1)), P(buf(2)), P(buf(3)), P(buf(4)), P(buf(5)),
                                      (const float*)P(buf(6)), (const float*)P(buf(7)), (float*)P(buf(8)), P(buf(9)),
@@ -173,6 +183,10 @@ int main(void) {
                                                        (const float*)pick_ptr(7), (float*)pick_ptr(8),
                                                        pick_ptr(9), pick_ptr(10), wsb, b, h, t, dd, l,
                                                        (ha_dtype)dt, upd, 0.0f, NULL));
+    expect_error(name, hybrid_attn_forward_mix(pick_ptr(0), pick_ptr(1), pick_ptr(2), pick_ptr(3), pick_ptr(4),
+                                               pick_ptr(5), (const float*)pick_ptr(6), (const float*)pick_ptr(7),
+                                               (float*)pick_ptr(8), pick_ptr(9), (const float*)pick_ptr(11),
+                                               pick_ptr(10), wsb, b, h, t, dd, l, (ha_dtype)dt, upd, 0.0f, NULL));
     expect_error(name, hybrid_attn_forward_noalloc(pick_ptr(0), pick_ptr(1), pick_ptr(2), pick_ptr(3),
                                                    pick_ptr(4), pick_ptr(5), (const float*)pick_ptr(6),
                                                    (const float*)pick_ptr(7), (float*)pick_ptr(8), pick_ptr(9), b,

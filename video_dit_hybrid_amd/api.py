@@ -21,7 +21,7 @@ EXPORTS = ("hybrid_attn_forward", "hybrid_attn_workspace_bytes", "hybrid_attn_in
            "hybrid_attn_gated_workspace_bytes", "hybrid_attn_gates", "hybrid_attn_gates_workspace_bytes",
            "hybrid_attn_kvcache_forward", "hybrid_attn_kvcache_workspace_bytes",
            "hybrid_attn_forward_token_level", "hybrid_attn_token_level_workspace_bytes",
-           "hybrid_attn_forward_noalloc", "hybrid_attn_noalloc_scratch_bytes")
+           "hybrid_attn_forward_noalloc", "hybrid_attn_noalloc_scratch_bytes", "hybrid_attn_forward_mix")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # HYBRID_ATTN_LIBRARY=debug selects the build with device index checks
@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     vp, i, sz, f, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_longlong
     L.hybrid_attn_forward.argtypes = [vp] * 10 + [vp, sz, i, i, i, i, i, i, i, f, vp]
     L.hybrid_attn_forward.restype = i
+    L.hybrid_attn_forward_mix.argtypes = [vp] * 11 + [vp, sz, i, i, i, i, i, i, i, f, vp]
+    L.hybrid_attn_forward_mix.restype = i
     L.hybrid_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.hybrid_attn_workspace_bytes.restype = sz
     L.hybrid_attn_intra_readout.argtypes = [vp, vp, vp, vp, vp, ll, ll, vp, i, i, i, i, i, i, f, vp]
@@ -186,21 +188,29 @@ def hybrid_attn_forward(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, upda
     """The layer call: returns out [B,T,H,d]; with update_state the fp32 state
     [B,H,d,d] is advanced in place to S_F, otherwise it is left unchanged.
     Layouts as in include/hybrid_attn.h. Asynchronous on the current stream."""
+    return _forward_call(lib().hybrid_attn_forward, "hybrid_attn_forward", q, k, v, qp, kp, vp, alpha, beta, state,
+                         frame_len, update_state, softmax_scale, out, workspace)
+
+
+def _forward_call(fn, name, q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, softmax_scale, out,
+                  workspace, mix=None):
+    """Checks, output and workspace allocation of a forward call, then the
+    call of fn (hybrid_attn_forward, or hybrid_attn_forward_mix with mix)."""
     torch = _torch()
     if q.device.type != "cuda":
-        raise ValueError("hybrid_attn_forward runs on a GPU; tensors must be on a cuda device")
+        raise ValueError(f"{name} runs on a GPU; tensors must be on a cuda device")
     B, T, H, d = q.shape
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
     F = T // frame_len if frame_len > 0 and T % frame_len == 0 else -1
     if F <= 0:
         raise ValueError(f"T={T} must be a positive multiple of frame_len={frame_len}")
-    for name, t in (("k", k), ("v", v), ("qp", qp)):
-        _check(name, t, (B, T, H, d), dt, dev)
+    for nm, t in (("k", k), ("v", v), ("qp", qp)):
+        _check(nm, t, (B, T, H, d), dt, dev)
     _check("state", state, (B, H, d, d), torch.float32, dev)
     if update_state:
-        for name, t in (("kp", kp), ("vp", vp)):
-            _check(name, t, (B, T, H, d), dt, dev)
+        for nm, t in (("kp", kp), ("vp", vp)):
+            _check(nm, t, (B, T, H, d), dt, dev)
         _check("alpha", alpha, (B, F, H), torch.float32, dev)
         _check("beta", beta, (B, T, H), torch.float32, dev)
     if out is None:
@@ -211,15 +221,28 @@ def hybrid_attn_forward(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, upda
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().hybrid_attn_forward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(qp), _ptr(kp if update_state else None),
-        _ptr(vp if update_state else None), _ptr(alpha if update_state else None),
-        _ptr(beta if update_state else None), _ptr(state), _ptr(out),
-        _ptr(workspace), ws_bytes, B, H, T, d, frame_len, code, int(bool(update_state)),
-        float(softmax_scale), _stream(dev))
+    head = [_ptr(q), _ptr(k), _ptr(v), _ptr(qp), _ptr(kp if update_state else None),
+            _ptr(vp if update_state else None), _ptr(alpha if update_state else None),
+            _ptr(beta if update_state else None), _ptr(state), _ptr(out)]
+    if mix is not None:
+        head.append(_ptr(mix))
+    st = fn(*head, _ptr(workspace), ws_bytes, B, H, T, d, frame_len, code, int(bool(update_state)),
+            float(softmax_scale), _stream(dev))
     if st != 0:
-        raise HybridAttnError(st, "hybrid_attn_forward")
+        raise HybridAttnError(st, name)
     return out
+
+
+def hybrid_attn_forward_mix(q, k, v, qp, kp, vp, alpha, beta, state, frame_len, update_state, mix,
+                            softmax_scale: float = 0.0, out=None, workspace=None):
+    """hybrid_attn_forward with per-branch output weights: mix fp32 [B, H, 2]
+    holds (w_softmax, w_inter) per (stream, head); out = w_softmax O_intra +
+    w_inter O_inter. bf16 only."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    _check("mix", mix, (B, H, 2), torch.float32, q.device)
+    return _forward_call(lib().hybrid_attn_forward_mix, "hybrid_attn_forward_mix", q, k, v, qp, kp, vp, alpha, beta,
+                         state, frame_len, update_state, softmax_scale, out, workspace, mix)
 
 
 def fmap_workspace_bytes(B, H, T, frame_len, d, update_state) -> int:

@@ -113,7 +113,7 @@ struct StepFlags {
   static constexpr bool NEXT = NEXT_, TAIL = TAIL_, LOADK = LOADK_;
 };
 
-template <int D, bool KV>
+template <int D, bool KV, bool MIX = false>
 __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ qp,
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     const unsigned char* __restrict__ sfrag, uint16_t* __restrict__ out, int H, int T, int L, int F,
     int qtiles, int n_items, float c2 /* softmax scale * log2(e) */,
     int Tk, int kv_off, int nsplit, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    const float* __restrict__ add_o) {
+    const float* __restrict__ add_o, const float* __restrict__ mix) {
   using C = Cfg<D>;
   constexpr int NCH = C::NCH;
   __shared__ __align__(16) unsigned char smem[C::SMEM];
@@ -470,6 +470,32 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     }
     return;
   } else {
+  // The readout Q'S goes into rd: o itself (the plain sum O/l + Q'S), or, with
+  // per-branch weights (MIX: mix[b, h] = (w_softmax, w_inter)), a separate
+  // accumulator, added as w_softmax O/l + w_inter Q'S.
+  f32x16 racc[MIX ? C::DB : 1];
+  f32x16* const rd = MIX ? racc : o;
+  float w_inter = 1.f;
+  auto mix_scale = [&](f32x16* oo, float l) {
+    float f = 1.f / l;
+    if constexpr (MIX) {
+      const float2 w = reinterpret_cast<const float2*>(mix)[b * H + h];
+      f *= w.x;
+      w_inter = w.y;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) racc[db] = f32x16{};
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) oo[db] *= f;
+  };
+  auto mix_add = [&](f32x16* oo) {
+    if constexpr (MIX) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oo[db][r] = fmaf(w_inter, racc[db][r], oo[db][r]);
+    }
+  };
   // ---- epilogue: O = O / l + Q' S_n. S_n reaches LDS either as the bf16
   // readout fragments the state scan wrote (copied as they are), or from the
   // fp32 row-major state, converted here to bf16 [dk][dv].
@@ -485,9 +511,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (!wave_active) return;
-    const float inv = 1.f / sum_across_halves(l0 + l1);
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) o[db] *= inv;
+    mix_scale(o, sum_across_halves(l0 + l1));
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       // contraction slot 8*hh + e holds dk = 16*ks + 8*(e/4) + 4*hh + e%4
@@ -497,9 +521,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (db * C::KSTEPS + ks) * 1024 + lane * 16);
-        o[db] = mfma32x32x16(a, bq, o[db]);
+        rd[db] = mfma32x32x16(a, bq, rd[db]);
       }
     }
+    mix_add(o);
   } else {
     // all of a thread's loads are issued before the first conversion, so
     // their latencies overlap instead of adding up
@@ -518,9 +543,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     }
     __syncthreads();
     if (!wave_active) return;
-    const float inv = 1.f / sum_across_halves(l0 + l1);
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) o[db] *= inv;
+    mix_scale(o, sum_across_halves(l0 + l1));
     // same contraction order as the fragment path (slot 8*hh + e <-> dk =
     // 16*ks + 8*(e/4) + 4*hh + e%4), so both paths give identical results:
     // the two transposed reads take rows 16*ks + 4*hh + i/4 and those + 8
@@ -538,9 +561,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
       for (int db = 0; db < C::DB; ++db) {
         const u32x2 x0 = ds_read_tr16(smem + s_off(16 * ks + srow, db));
         const u32x2 x1 = ds_read_tr16(smem + s_off(16 * ks + 8 + srow, db));
-        o[db] = mfma32x32x16(u32x4{x0[0], x0[1], x1[0], x1[1]}, bq, o[db]);
+        rd[db] = mfma32x32x16(u32x4{x0[0], x0[1], x1[0], x1[1]}, bq, rd[db]);
       }
     }
+    mix_add(o);
   }
   if (my_q < L) {
     uint16_t* op = out + fbase + (long long)my_q * H * D;
@@ -609,23 +633,28 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u32x4* __restrict_
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const void* qp,
                             const float* states, long long stride_bh, long long stride_frame,
                             const void* sfrag, void* out, const Shape& s, float scale,
-                            hipStream_t st) {
+                            hipStream_t st, const float* mix) {
   const int qtiles = (s.L + QPB - 1) / QPB;
   const long long items = (long long)s.B * s.H * s.F * qtiles;
   const int grid = (int)((items + 7) / 8 * 8);
   const float c2 = scale * kLog2e;
   HA_LOG("launch attn_bf16_kernel<%d>: grid %d x %d threads (%lld items = %d streams x %d heads x %d frames x %d "
-         "query tiles of %d; key tiles of %d, %d KiB LDS; readout from %s)",
+         "query tiles of %d; key tiles of %d, %d KiB LDS; readout from %s%s)",
          s.d, grid, NT, items, s.B, s.H, s.F, qtiles, QPB, KT, (s.d == 128 ? Cfg<128>::SMEM : Cfg<64>::SMEM) >> 10,
-         sfrag ? "bf16 fragments" : "fp32 states");
+         sfrag ? "bf16 fragments" : "fp32 states", mix ? "; per-branch weights" : "");
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                               (const uint16_t*)qp, states, stride_bh, stride_frame,
                               (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
-                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr);
+                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr, mix);
   };
-  if (s.d == 128) args(attn_bf16_kernel<128, false>);
-  else args(attn_bf16_kernel<64, false>);
+  if (mix) {
+    if (s.d == 128) args(attn_bf16_kernel<128, false, true>);
+    else args(attn_bf16_kernel<64, false, true>);
+  } else {
+    if (s.d == 128) args(attn_bf16_kernel<128, false>);
+    else args(attn_bf16_kernel<64, false>);
+  }
   return hipGetLastError();
 }
 
@@ -653,7 +682,7 @@ hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
                               nullptr, 0, 0, nullptr, (uint16_t*)out, s.H, s.T, s.L, s.F, qtiles, units, c2, Tk,
-                              kv_off, nsplit, part_o, (float2*)part_ml, add_o);
+                              kv_off, nsplit, part_o, (float2*)part_ml, add_o, nullptr);
   };
   if (s.d == 128) args(attn_bf16_kernel<128, true>);
   else args(attn_bf16_kernel<64, true>);

@@ -16,10 +16,12 @@ struct Shape {
 // hybrid_attn.h), or, when sfrag is not null, d x d bf16 readout fragments
 // (the layout state_scan writes, below) at sfrag + (b*H + h)*stride_bh +
 // n*stride_frame, the two strides then counted in bytes.
+// mix, if not null: fp32 [B, H, 2] weights (w_softmax, w_inter) per (stream,
+// head); the output is then w_softmax O/l + w_inter Q'S instead of the sum.
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const void* qp,
                             const float* states, long long stride_bh, long long stride_frame,
                             const void* sfrag, void* out, const Shape& s, float scale,
-                            hipStream_t st);
+                            hipStream_t st, const float* mix = nullptr);
 
 // KV mode of the same kernel (the softmax teacher with a full KV cache): the
 // queries of call frame n (q, out [B, T, H, d], T = F * L) attend to the keys

@@ -146,9 +146,9 @@ ha_status launched(hipError_t e) { return e == hipSuccess ? HA_OK : HA_ERR_DEVIC
 ha_status run_readout(const void* q, const void* k, const void* v, const void* qp,
                       const float* states, long long sbh, long long sfr, void* out,
                       const ha::Shape& s, int dtype, float scale, hipStream_t st,
-                      const void* sfrag = nullptr) {
+                      const void* sfrag = nullptr, const float* mix = nullptr) {
   if (dtype == HA_BF16)
-    return launched(ha::launch_attn_bf16(q, k, v, qp, states, sbh, sfr, sfrag, out, s, scale, st));
+    return launched(ha::launch_attn_bf16(q, k, v, qp, states, sbh, sfr, sfrag, out, s, scale, st, mix));
   return launched(ha::launch_attn_fp32(q, k, v, qp, states, sbh, sfr, out, s, scale, st));
 }
 
@@ -176,6 +176,7 @@ struct ForwardArgs {
   ha_dtype dtype;
   int update_state;
   float softmax_scale;
+  const float* mix;  // per-branch output weights [B, H, 2], or null (the plain sum)
 };
 
 // Checks of a forward call that do not involve the workspace; on success
@@ -191,6 +192,8 @@ ha_status validate_forward(const ForwardArgs& a, ha::Shape* s, size_t* need) {
   if (a.update_state &&
       (!aligned(a.kp, 16) || !aligned(a.vp, 16) || !aligned(a.alpha, 4) || !aligned(a.beta, 4)))
     return HA_ERR_ALIGN;
+  if (a.mix && a.dtype != HA_BF16) return HA_ERR_UNSUPPORTED;
+  if (a.mix && !aligned(a.mix, 8)) return HA_ERR_ALIGN;
   *need = hybrid_attn_workspace_bytes(a.B, a.H, a.T, a.frame_len, a.d, a.update_state);
   return HA_OK;
 }
@@ -200,11 +203,13 @@ bool workspace_overlaps(const ForwardArgs& a, const ha::Shape& s, const void* ws
   const size_t tb = tensor_bytes(s, a.dtype);
   const size_t stb = (size_t)a.B * a.H * (size_t)a.d * a.d * sizeof(float);
   const size_t ab = (size_t)a.B * s.F * a.H * sizeof(float), bb = (size_t)a.B * a.T * a.H * sizeof(float);
+  const size_t mb = a.mix ? (size_t)a.B * a.H * 2 * sizeof(float) : 0;
   if (a.update_state)
     return written_overlaps({{a.out, tb}, {a.state, stb}, {ws, need}},
                             {{a.q, tb}, {a.k, tb}, {a.v, tb}, {a.qp, tb}, {a.kp, tb}, {a.vp, tb}, {a.alpha, ab},
-                             {a.beta, bb}});
-  return written_overlaps({{a.out, tb}}, {{a.q, tb}, {a.k, tb}, {a.v, tb}, {a.qp, tb}, {a.state, stb}});
+                             {a.beta, bb}, {a.mix, mb}});
+  return written_overlaps({{a.out, tb}},
+                          {{a.q, tb}, {a.k, tb}, {a.v, tb}, {a.qp, tb}, {a.state, stb}, {a.mix, mb}});
 }
 
 // Workspace of a forward call: the state update's increments and, over
@@ -220,11 +225,12 @@ size_t forward_base_bytes(const ha::Shape& s, int update_state) {
 ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspace, hipStream_t st) {
   const float scale = resolve_scale(a.softmax_scale, a.d);
   const long long dd = (long long)a.d * a.d;
-  if (!a.update_state) return run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st);
+  if (!a.update_state)
+    return run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st, nullptr, a.mix);
   float* gram = (float*)workspace;
   const size_t nstate = (size_t)s.B * s.H * (size_t)dd;
   if (s.F == 1) {
-    ha_status r = run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st);
+    ha_status r = run_readout(a.q, a.k, a.v, a.qp, a.state, dd, 0, a.out, s, a.dtype, scale, st, nullptr, a.mix);
     if (r != HA_OK) return r;
     r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st);
     return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
@@ -236,7 +242,8 @@ ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspa
     ha_status r = run_update(a.kp, a.vp, a.alpha, a.beta, a.state, nullptr, gram, s, a.dtype, st, snap_area);
     if (r != HA_OK) return r;
     const long long fb = (long long)s.d * s.d * 2;  // fragment bytes per frame
-    r = run_readout(a.q, a.k, a.v, a.qp, nullptr, (long long)s.F * fb, fb, a.out, s, a.dtype, scale, st, snap_area);
+    r = run_readout(a.q, a.k, a.v, a.qp, nullptr, (long long)s.F * fb, fb, a.out, s, a.dtype, scale, st, snap_area,
+                    a.mix);
     return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
   }
   float* snaps = (float*)snap_area;
@@ -377,6 +384,27 @@ ha_status hybrid_attn_forward(const void* q, const void* k, const void* v, const
   log_call("hybrid_attn_forward", s, dtype, update_state, need);
   return debug_finish("hybrid_attn_forward",
                       launch_forward(a, s, workspace, (hipStream_t)stream), (hipStream_t)stream);
+}
+
+ha_status hybrid_attn_forward_mix(const void* q, const void* k, const void* v, const void* qp,
+                                  const void* kp, const void* vp, const float* alpha,
+                                  const float* beta, float* state, void* out, const float* mix,
+                                  void* workspace, size_t workspace_bytes, int B, int H, int T, int d,
+                                  int frame_len, ha_dtype dtype, int update_state, float softmax_scale,
+                                  void* stream) {
+  const ForwardArgs a{q, k, v, qp, kp, vp, alpha, beta, state, out, B, H, T, d, frame_len, dtype, update_state,
+                      softmax_scale, mix};
+  ha::Shape s;
+  size_t need = 0;
+  if (!mix) return check_shape(B, H, T, d, frame_len, dtype, &s) != HA_OK ? HA_ERR_SHAPE : HA_ERR_NULL;
+  ha_status r = validate_forward(a, &s, &need);
+  if (r != HA_OK) return r;
+  if (update_state && !aligned(workspace, 16)) return HA_ERR_ALIGN;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return HA_ERR_WORKSPACE;
+  if (workspace_overlaps(a, s, workspace, need)) return HA_ERR_ALIAS;
+  log_call("hybrid_attn_forward_mix", s, dtype, update_state, need);
+  return debug_finish("hybrid_attn_forward_mix", launch_forward(a, s, workspace, (hipStream_t)stream),
+                      (hipStream_t)stream);
 }
 
 }  // extern "C"

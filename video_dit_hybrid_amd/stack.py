@@ -12,6 +12,12 @@ layers evenly (layer_kinds). There are no projection weights either, so every
 layer of a pass reads the same q, k, v (and q', k', v', alpha, beta): the work
 of each layer is that of a real layer of this shape, the values are not.
 
+Optionally every hybrid layer weights its two branches (mix_weights): LinVideo
+trains a per-layer r with o = r SoftmaxAttn + (1 - r) LinearAttn, SALAD scales
+the linear branch by a sigmoid s computed from the input and the timestep. A
+layer's weights are one fp32 [B, H, 2] tensor of (w_softmax, w_inter) per
+(stream, head); without trained models they are synthetic.
+
 All the arithmetic runs in the HIP library through the C ABI (api.py); this
 module only owns the per-layer buffers and the call order.
 """
@@ -36,9 +42,15 @@ class AttentionStack:
     frames. run_frame(n, passes) runs one frame's passes (denoising passes,
     then the clean pass, the last of `passes`) through every layer."""
 
-    def __init__(self, kinds, B, H, d, frame_len, max_frames, device="cuda"):
+    def __init__(self, kinds, B, H, d, frame_len, max_frames, device="cuda", mix_weights=None):
+        """mix_weights: None (hybrid layers output the plain sum of the two
+        branches) or one fp32 [B, H, 2] tensor per layer (entries of softmax
+        layers are ignored): (w_softmax, w_inter) for hybrid_attn_forward_mix."""
         import torch
         self.kinds = list(kinds)
+        if mix_weights is not None and len(mix_weights) != len(self.kinds):
+            raise ValueError("mix_weights needs one entry per layer")
+        self.mix = list(mix_weights) if mix_weights is not None else [None] * len(self.kinds)
         self.B, self.H, self.d, self.L, self.max_frames = B, H, d, frame_len, max_frames
         self.states, self.caches = [], []
         for kind in self.kinds:
@@ -66,14 +78,15 @@ class AttentionStack:
         last = len(passes) - 1
         for p, t in enumerate(passes):
             clean = p == last
-            for kind, st, cache in zip(self.kinds, self.states, self.caches):
+            for kind, st, cache, mix in zip(self.kinds, self.states, self.caches, self.mix):
                 if kind == "hybrid":
-                    if clean:
-                        api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], t["kp"], t["vp"], t["alpha"],
-                                                t["beta"], st, self.L, 1, out=out, workspace=self.hws)
+                    upd = (t["kp"], t["vp"], t["alpha"], t["beta"]) if clean else (None, None, None, None)
+                    if mix is None:
+                        api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], *upd, st, self.L, int(clean),
+                                                out=out, workspace=self.hws)
                     else:
-                        api.hybrid_attn_forward(t["q"], t["k"], t["v"], t["qp"], None, None, None, None, st,
-                                                self.L, 0, out=out, workspace=self.hws)
+                        api.hybrid_attn_forward_mix(t["q"], t["k"], t["v"], t["qp"], *upd, st, self.L, int(clean),
+                                                    mix, out=out, workspace=self.hws)
                 else:
                     api.hybrid_attn_kvcache_forward(t["q"], t["k"], t["v"], cache[0], cache[1], self.L, n, out=out,
                                                     workspace=self.kws)
