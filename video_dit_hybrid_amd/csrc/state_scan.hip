@@ -39,7 +39,7 @@ constexpr int CWM = 32;   // state columns per work-group
 template <int D>
 __global__ __launch_bounds__((D / 32 + 1) * 64) void state_scan_mfma_kernel(
     const unsigned char* __restrict__ ws, const float* __restrict__ alpha, float* __restrict__ state,
-    float* __restrict__ snaps, u32x4* __restrict__ sfrag, int H, int F) {
+    float* __restrict__ snaps, u32x4* __restrict__ sfrag, int H, int F, int n_items) {
   constexpr int NRB = D / 32;                       // 32-row bands (= compute waves)
   constexpr int NCB = D / CWM;
   constexpr int KS = D / 16;                        // k-steps over d_k
@@ -51,8 +51,13 @@ __global__ __launch_bounds__((D / 32 + 1) * 64) void state_scan_mfma_kernel(
   __shared__ __align__(16) unsigned char gbuf[2][GB];
   __shared__ __align__(16) u32x4 lds[2][2][KS][64];
 
-  const int cb = blockIdx.x % NCB;
-  const int bh = blockIdx.x / NCB;
+  // the column blocks of one (b, h) are consecutive items on one XCD (the
+  // grid gives each XCD a multiple of NCB items), so the four work-groups
+  // reading the same -G of a frame share that XCD's L2
+  const int item = xcd_major_item(gridDim.x);
+  if (item >= n_items) return;
+  const int cb = item % NCB;
+  const int bh = item / NCB;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -246,15 +251,19 @@ HA_DEBUG_READER(debug_take_scan)
 
 hipError_t launch_state_scan_bf16(const void* ws, const float* alpha, float* state, float* snapshots,
                                   void* sfrag, const Shape& s, hipStream_t st) {
-  const int groups = s.B * s.H * (s.d / CWM);
-  HA_LOG("launch state_scan_mfma_kernel<%d>: grid %d x %d threads (%d frames in sequence; snapshots %s)", s.d,
-         groups, (s.d / 32 + 1) * 64, s.F, sfrag ? "as bf16 readout fragments" : snapshots ? "fp32" : "none");
+  const int ncb = s.d / CWM;
+  const int items = s.B * s.H * ncb;
+  const int per_xcd = (items + 8 * ncb - 1) / (8 * ncb) * ncb;  // whole (b, h) units per XCD
+  const int grid = 8 * per_xcd;
+  HA_LOG("launch state_scan_mfma_kernel<%d>: grid %d x %d threads (%d (b, h, column block) items, %d per XCD; %d "
+         "frames in sequence; snapshots %s)", s.d, grid, (s.d / 32 + 1) * 64, items, per_xcd, s.F,
+         sfrag ? "as bf16 readout fragments" : snapshots ? "fp32" : "none");
   if (s.d == 128)
-    state_scan_mfma_kernel<128><<<groups, (128 / 32 + 1) * 64, 0, st>>>(
-        (const unsigned char*)ws, alpha, state, snapshots, (u32x4*)sfrag, s.H, s.F);
+    state_scan_mfma_kernel<128><<<grid, (128 / 32 + 1) * 64, 0, st>>>(
+        (const unsigned char*)ws, alpha, state, snapshots, (u32x4*)sfrag, s.H, s.F, items);
   else
-    state_scan_mfma_kernel<64><<<groups, (64 / 32 + 1) * 64, 0, st>>>(
-        (const unsigned char*)ws, alpha, state, snapshots, (u32x4*)sfrag, s.H, s.F);
+    state_scan_mfma_kernel<64><<<grid, (64 / 32 + 1) * 64, 0, st>>>(
+        (const unsigned char*)ws, alpha, state, snapshots, (u32x4*)sfrag, s.H, s.F, items);
   return hipGetLastError();
 }
 
