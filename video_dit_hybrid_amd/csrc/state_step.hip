@@ -87,6 +87,7 @@ __device__ __forceinline__ int take_ticket(unsigned long long* t, unsigned long 
       return last;
     cur = seen;
   }
+  HA_CHECK(false, 8);  // debug bit 8: the exchange loop ran out (cannot happen with nsplit <= 16 splits)
   return 0;
 }
 
