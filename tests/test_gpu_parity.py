@@ -78,7 +78,7 @@ def test_tiny_shape_bf16_path():
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("L,F,B,H", [(1, 3, 1, 2), (17, 3, 2, 1), (64, 2, 1, 2), (100, 3, 1, 3),
-                                     (129, 2, 1, 1), (256, 2, 1, 2)])
+                                     (129, 2, 1, 1), (256, 2, 1, 2), (160, 3, 1, 1), (24, 1, 1, 3)])
 def test_edge_frame_lengths(dtype, d, L, F, B, H):
     w = small("480p", B=B, H=H, d=d, L=L, frames=F, dtype=dtype, state0_sigma=0.05)
     say(f"case edge dtype={dtype} d={d} L={L} F={F} B={B} H={H}")
