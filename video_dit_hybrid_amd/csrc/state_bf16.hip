@@ -13,6 +13,8 @@
 // (they are the inputs), but beta*K' is not; it is split into hi + lo bf16
 // parts (hi = bf16(x), lo = bf16(x - hi)), which carries ~16 mantissa bits,
 // and both parts are accumulated on MFMA in fp32.
+#include <type_traits>
+
 #include "ha_device.h"
 #include "ha_dma.h"
 #include "ha_launch.h"
@@ -26,10 +28,17 @@ constexpr int TC = 64;   // tokens per LDS chunk
 constexpr int NW = 8;    // waves per work-group
 constexpr int NT = NW * kWave;
 
-// grid: one work-group per (b, h, frame). Wave w owns the 32-row band
-// rb = w % (d/32) of both G = K'^T diag(beta) K' and B = K'^T diag(beta) V'
-// (the two share their A operand (beta K')^T), and the k-steps kh = w / (d/32)
-// of every 64-token chunk; the token halves are summed through LDS at the end.
+// grid: one work-group per (b, h, frame). Each wave owns one 32-row band rb
+// of both G = K'^T diag(beta) K' and B = K'^T diag(beta) V' (the two share
+// their A operand (beta K')^T) and one share kh of the k-steps of every
+// 64-token chunk; the token shares are summed through LDS at the end.
+//
+// G is symmetric. When the work-group writes the scan's format (not partial
+// sums), band rb computes only the G blocks (rb, cb >= rb), 10 of 16 at d =
+// 128, and the fragments of a lower block (cb, rb) come from the upper block
+// (rb, cb), transposed through LDS inside the wave that holds it. The bands
+// then carry unequal work (8, 7, 6, 5 blocks per k-step at d = 128), so the
+// waves that share a SIMD (w and w + 4) take a heavy and a light band.
 //
 // The K', V' chunks arrive row-major ([token][d] bf16, as stored) by direct
 // global -> LDS loads, three chunks in flight, and beta by a 4-byte-per-lane
@@ -78,8 +87,13 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
-  const int rb = wave % NRB;                 // row band of G and B
-  const int kh = wave / NRB;                 // which k-steps of each chunk
+  // row band of G and B, and which k-steps of each chunk: waves w and w + 4
+  // (one SIMD) hold bands 0 and 3 or 1 and 2 at d = 128, bands 0 and 1 at 64
+  static_assert(NRB == 4 || NRB == 2, "band pairing");
+  const int rb = NRB == 4 ? ((wave & 1) ^ (3 * (wave >> 2))) : (wave >> 2);
+  const int kh = NRB == 4 ? ((wave >> 1) & 1) : (wave & 3);
+  // only the upper-triangle G blocks, when writing the scan's format
+  const bool tri = !TWO && partial == nullptr;
 
   const uint32_t rsb = (uint32_t)H * D * 2;
   const long long fbase = ((long long)b * T + (long long)n * L) * ((long long)H * D) + (long long)h * D;
@@ -144,62 +158,81 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
            1);
   HA_CHECK(tr_off(16 * (KSC - 1) + 4, NRB - 1) + 8 <= TILE, 2);
   for (int c = 0; c < NBUF - 1 && c < nch; ++c) issue(c0 + c, c);
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c % NBUF;
-    // chunk c landed: at most the loads of the chunks after it are outstanding
-    const int later = (nch - 1 - c) < (NBUF - 2) ? (nch - 1 - c) : (NBUF - 2);
-    if (has_beta) {
-      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (2 * MY_SEGS + 1)));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS + 1));
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-    } else {
-      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * 2 * MY_SEGS));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS));
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-    __syncthreads();
-    // the buffer of chunk c-1 is free (every wave passed the barrier above
-    // after consuming it): refill it with chunk c+NBUF-1
-    if (c + NBUF - 1 < nch) issue(c0 + c + NBUF - 1, (c + NBUF - 1) % NBUF);
-    const unsigned char* kt = smem + buf * BUF;
-    const unsigned char* vt = kt + TILE;
-    const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
-    const float* be2 = be + (TWO ? TC : 0);
+  // TB < 0: every G block; TB >= 0: this wave's band is TB, G blocks cb >= TB
+  auto chunks = [&](auto tb_c) {
+    constexpr int TB = decltype(tb_c)::value;
+    const int band = TB >= 0 ? TB : rb;
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c % NBUF;
+      // chunk c landed: at most the loads of the chunks after it are outstanding
+      const int later = (nch - 1 - c) < (NBUF - 2) ? (nch - 1 - c) : (NBUF - 2);
+      if (has_beta) {
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (2 * MY_SEGS + 1)));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS + 1));
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+      } else {
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * 2 * MY_SEGS));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS));
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      __syncthreads();
+      // the buffer of chunk c-1 is free (every wave passed the barrier above
+      // after consuming it): refill it with chunk c+NBUF-1
+      if (c + NBUF - 1 < nch) issue(c0 + c + NBUF - 1, (c + NBUF - 1) % NBUF);
+      const unsigned char* kt = smem + buf * BUF;
+      const unsigned char* vt = kt + TILE;
+      const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
+      const float* be2 = be + (TWO ? TC : 0);
 #pragma unroll
-    for (int kk = 0; kk < KSC / KH; ++kk) {
-      const int ks = kh * (KSC / KH) + kk;
-      // A = (beta K')^T rows 32*rb.., tokens 16*ks + 8*hh + e: split hi + lo,
-      // shared by the G blocks (B operand K') and the B blocks (B operand V');
-      // with two step-size vectors the B blocks take their own (beta2 K')^T
-      const u32x4 kraw = tr8(kt, ks, rb);
-      auto scaled_split = [&](const float* bp, u32x4& hi4, u32x4& lo4) {
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh + 4);
+      for (int kk = 0; kk < KSC / KH; ++kk) {
+        const int ks = kh * (KSC / KH) + kk;
+        // A = (beta K')^T rows 32*rb.., tokens 16*ks + 8*hh + e: split hi + lo,
+        // shared by the G blocks (B operand K') and the B blocks (B operand V');
+        // with two step-size vectors the B blocks take their own (beta2 K')^T
+        const u32x4 kraw = tr8(kt, ks, band);
+        auto scaled_split = [&](const float* bp, u32x4& hi4, u32x4& lo4) {
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh + 4);
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const float bl = w2 < 2 ? b0[2 * w2] : b1[2 * w2 - 4];
-          const float bu = w2 < 2 ? b0[2 * w2 + 1] : b1[2 * w2 - 3];
-          const float x0 = bl * bf16_lo_to_f32(kraw[w2]);
-          const float x1 = bu * bf16_hi_to_f32(kraw[w2]);
-          const uint32_t hi = pack_bf16x2(x0, x1);
-          hi4[w2] = hi;
-          lo4[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+          for (int w2 = 0; w2 < 4; ++w2) {
+            const float bl = w2 < 2 ? b0[2 * w2] : b1[2 * w2 - 4];
+            const float bu = w2 < 2 ? b0[2 * w2 + 1] : b1[2 * w2 - 3];
+            const float x0 = bl * bf16_lo_to_f32(kraw[w2]);
+            const float x1 = bu * bf16_hi_to_f32(kraw[w2]);
+            const uint32_t hi = pack_bf16x2(x0, x1);
+            hi4[w2] = hi;
+            lo4[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+          }
+        };
+        u32x4 ahi, alo, bhi, blo;
+        scaled_split(be, ahi, alo);
+        if constexpr (TWO) scaled_split(be2, bhi, blo);
+        else { bhi = ahi; blo = alo; }
+#pragma unroll
+        for (int cb = 0; cb < NRB; ++cb) {
+          const u32x4 bv = tr8(vt, ks, cb);
+          if (TB < 0 || cb >= TB) {
+            const u32x4 bk = tr8(kt, ks, cb);
+            ag[cb] = mfma32x32x16(ahi, bk, ag[cb]);
+            ab[cb] = mfma32x32x16(bhi, bv, ab[cb]);
+            ag[cb] = mfma32x32x16(alo, bk, ag[cb]);
+            ab[cb] = mfma32x32x16(blo, bv, ab[cb]);
+          } else {
+            ab[cb] = mfma32x32x16(bhi, bv, ab[cb]);
+            ab[cb] = mfma32x32x16(blo, bv, ab[cb]);
+          }
         }
-      };
-      u32x4 ahi, alo, bhi, blo;
-      scaled_split(be, ahi, alo);
-      if constexpr (TWO) scaled_split(be2, bhi, blo);
-      else { bhi = ahi; blo = alo; }
-#pragma unroll
-      for (int cb = 0; cb < NRB; ++cb) {
-        const u32x4 bk = tr8(kt, ks, cb);
-        const u32x4 bv = tr8(vt, ks, cb);
-        ag[cb] = mfma32x32x16(ahi, bk, ag[cb]);
-        ab[cb] = mfma32x32x16(bhi, bv, ab[cb]);
-        ag[cb] = mfma32x32x16(alo, bk, ag[cb]);
-        ab[cb] = mfma32x32x16(blo, bv, ab[cb]);
       }
     }
+  };
+  // the band as a compile-time constant, so that each band's loop holds
+  // exactly its MFMAs
+  if (!tri) chunks(std::integral_constant<int, -1>{});
+  else if (rb == 0) chunks(std::integral_constant<int, 0>{});
+  else if (rb == 1) chunks(std::integral_constant<int, 1>{});
+  else if constexpr (NRB > 2) {
+    if (rb == 2) chunks(std::integral_constant<int, 2>{});
+    else chunks(std::integral_constant<int, 3>{});
   }
 
   // sum the token halves: waves with kh > 0 hand their partial blocks to the
@@ -207,7 +240,7 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   if constexpr (KH > 1) {
     __syncthreads();  // every wave is done with the chunk buffers
     f32x4* part = reinterpret_cast<f32x4*>(smem);
-    if (kh > 0) {
+    if (kh > 0) {  // (with tri, the lower G blocks are zero and not read)
       f32x4* my = part + ((size_t)((kh - 1) * NRB + rb) * NRB * 2 * 4) * 64;
 #pragma unroll
       for (int cb = 0; cb < NRB; ++cb)
@@ -252,17 +285,44 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   // workspace order [b][h][frame] (the grid runs heads fastest)
   unsigned char* base = reinterpret_cast<unsigned char*>(gram) +
                         ((size_t)(b * H + h) * F + n) * (size_t)D * D * 8;
+  // the lower block (cb, rb) of G is the transpose of the upper block (rb,
+  // cb): it goes through 32 x 36 floats of LDS (rows padded to keep the
+  // 16-byte reads aligned), the region whose partial sums this wave has read
+  float* tp = reinterpret_cast<float*>(smem) + (size_t)rb * NRB * 2 * 4 * 64 * 4;
+  const int lr = lane & 31;
 #pragma unroll
   for (int cb = 0; cb < NRB; ++cb) {
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4)
       store_b4<D>(base, rb, cb, v4, lane, f32x4{ab[cb][4 * v4], ab[cb][4 * v4 + 1], ab[cb][4 * v4 + 2], ab[cb][4 * v4 + 3]});
+    if (tri && cb < rb) continue;
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
       float g8[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) g8[e] = ag[cb][8 * sh + e];
       store_g_half<D>(base, rb, cb, sh, lane, g8);
+    }
+    if (tri && cb > rb) {
+      // element r of lane l is G(rb, cb)[x_r][l % 32], x_r = 8(r/4) + 4hh + r%4;
+      // the lower block wants element r of lane l = G(rb, cb)[l % 32][x_r]
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // earlier reads of the region returned
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tp[(8 * (r >> 2) + 4 * hh + (r & 3)) * 36 + lr] = ag[cb][r];
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      asm volatile("" ::: "memory");
+      float t16[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(tp + lr * 36 + 8 * q4 + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t16[4 * q4 + e] = x[e];
+      }
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) store_g_half<D>(base, cb, rb, sh, lane, t16 + 8 * sh);
     }
   }
 }
