@@ -838,14 +838,20 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the per-step spread from a second pass of K steps: a timing event
+    # between two calls leaves a few microseconds of idle GPU, so the pass
+    # that gives ms_per_step records none
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     sev[0].record(stream)
     for i in range(args.steps):
         step()
         sev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
     step_ms = sorted(sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps))
 
     # dominant kernel alone: intra-frame attention + readout over all frames,
