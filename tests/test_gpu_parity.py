@@ -89,6 +89,36 @@ def test_edge_frame_lengths(dtype, d, L, F, B, H):
         assert eo < 1e-5 and es < 1e-5
 
 
+# --- ragged lengths with more than 256 attention work-groups ------------------
+# (launches of up to 256 work-groups, as in every test above, take the
+# attention kernel with a loader wave; these take the one without)
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,F,H", [(1, 33, 8), (17, 33, 8), (129, 17, 8), (200, 17, 8)])
+def test_edge_lengths_without_loader_wave(d, L, F, H):
+    w = small("480p", B=1, H=H, d=d, L=L, frames=F, state0_sigma=0.05)
+    qtiles = (L + 127) // 128
+    assert w.B * w.H * w.frames * qtiles > 256
+    say(f"case edge, no loader wave, d={d} L={L} F={F} H={H}")
+    eo, es, *_ = full_compare(w)
+    say(f"  rel_err out {eo:.3e} state {es:.3e}")
+    assert eo < TOL_OUT and es < TOL_STATE
+
+
+# --- many frames: one gram work-group per (stream, head, frame) ----------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_frames_unsplit_gram(d):
+    # 8 heads x 16 frames = 128 units: each frame's increments come from one
+    # work-group computing the upper-triangle blocks of G (4 chunks of 64
+    # tokens per frame, the last ragged), not from split partial sums
+    w = small("480p", B=1, H=8, d=d, L=200, frames=16, state0_sigma=0.05)
+    say(f"case many frames, unsplit gram, d={d}")
+    eo, es, *_ = full_compare(w)
+    say(f"  rel_err out {eo:.3e} state {es:.3e}")
+    assert eo < TOL_OUT and es < TOL_STATE
+
+
 # --- one frame per call: the state write as one kernel (d = 128) -------------
 
 @pytest.mark.parametrize("L,B,H,d", [(1560, 1, 12, 128), (1560, 1, 2, 128), (1000, 1, 1, 128), (513, 1, 1, 128),

@@ -40,6 +40,12 @@
 // result does not depend on that choice: a reference point common to the
 // numerator and the denominator cancels.
 //
+// Loader wave (LOADER): when the launch has at most one work-group per CU
+// (one frame of few heads), a work-group runs alone and its waves would stall
+// issuing their share of each step's 32 KB of tile copies (the address unit
+// takes 64 bytes per clock). A fifth wave then issues every copy and the four
+// compute waves only compute; the step barrier still orders the buffers.
+//
 // KV mode (the softmax teacher with a full KV cache that the hybrid layer
 // replaces, ARL2 section 1): the same kernel with frame n's queries attending
 // to the keys [0, kv_off + (n+1) L) of a key/value cache, no readout. The keys
@@ -63,6 +69,7 @@ constexpr int NW = 4;           // waves per work-group
 constexpr int QPB = QPW * NW;   // queries per work-group
 constexpr int NT = NW * kWave;  // threads per work-group
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kLoaderMaxGroups = 256;  // launches up to this many work-groups take the loader wave
 
 template <int D>
 struct Cfg {
@@ -113,8 +120,8 @@ struct StepFlags {
   static constexpr bool NEXT = NEXT_, TAIL = TAIL_, LOADK = LOADK_;
 };
 
-template <int D, bool KV, bool MIX = false>
-__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
+template <int D, bool KV, bool MIX = false, bool LOADER = false>
+__global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ qp,
     const float* __restrict__ states, long long stride_bh, long long stride_frame,
@@ -156,6 +163,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int lr = lane & 31, hh = lane >> 5;
+  static_assert(!(KV && LOADER), "the loader wave serves the readout kernel only");
+  const bool is_loader = LOADER && wave == NW;
   // debug bit 1: the work item decodes to a valid (b, h, frame, query tile, split)
   HA_CHECK(qt >= 0 && qt < qtiles && h >= 0 && h < H && n >= 0 && n < F && b >= 0 && sp >= 0 && sp < nsplit, 1);
   const uint32_t rsb = (uint32_t)H * D * 2;  // bytes between consecutive tokens
@@ -184,8 +193,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     return rsrc_words(base + kvbase + (long long)(t0 + j) * KT * H * D, (int)((uint32_t)(rows - 1) * rsb + D * 2));
   };
 
-  const int q0 = qt * QPB + wave * QPW;
-  const bool wave_active = q0 < L;
+  const int q0 = qt * QPB + (is_loader ? 0 : wave) * QPW;
+  const bool wave_active = !is_loader && q0 < L;
   const int my_q = q0 + lr;
 
   // ---- direct-to-LDS tile loads. Load i of wave w fills the 1 KB LDS segment
@@ -197,29 +206,41 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
   constexpr int ROWS_PER_SEG = 64 / NCH;
   constexpr int SEG_ROW_STEP = NW * ROWS_PER_SEG;  // rows between a wave's segments
   static_assert(SEG_ROW_STEP % 8 == 0 || NCH < 16, "segment step must keep the swizzle");
-  uint32_t koff0, voff0;
-  {
-    const int row = wave * ROWS_PER_SEG + lane / NCH, pc = lane % NCH;
-    koff0 = row * rsb + ((pc ^ k_swz<NCH>(row)) << 4);
-    voff0 = row * rsb + ((pc ^ v_swz<NCH>(row)) << 4);
+  // the load sets a wave issues: its own (set w = wave), or with a loader
+  // wave all NW sets, from the loader
+  constexpr int NSETS = LOADER ? NW : 1;
+  uint32_t koff[NSETS], voff[NSETS];
+#pragma unroll
+  for (int s2 = 0; s2 < NSETS; ++s2) {
+    const int row = (LOADER ? s2 : wave) * ROWS_PER_SEG + lane / NCH, pc = lane % NCH;
+    koff[s2] = row * rsb + ((pc ^ k_swz<NCH>(row)) << 4);
+    voff[s2] = row * rsb + ((pc ^ v_swz<NCH>(row)) << 4);
   }
   // The copies are inline asm: the compiler cannot tell which LDS bytes a
   // builtin copy writes and would wait for every copy in flight before each
   // later LDS read; with these, a tile's copies stay in flight until the wait
   // at the end of the step.
   auto issue_k = [&](int j, int buf) {
+    if (LOADER && !is_loader) return;
     const uint32_t toff = KV ? 0u : (uint32_t)j * KT * rsb;
     const u32x4 r = KV ? tile_rsrc(k, j) : rk;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16_asm(r, lds0 + buf * C::TILE + (i * NW + wave) * 1024, koff0, toff + i * SEG_ROW_STEP * rsb);
+#pragma unroll
+      for (int s2 = 0; s2 < NSETS; ++s2)
+        dma16_asm(r, lds0 + buf * C::TILE + (i * NW + (LOADER ? s2 : wave)) * 1024, koff[s2],
+                  toff + i * SEG_ROW_STEP * rsb);
   };
   auto issue_v = [&](int j, int buf) {
+    if (LOADER && !is_loader) return;
     const uint32_t toff = KV ? 0u : (uint32_t)j * KT * rsb;
     const u32x4 r = KV ? tile_rsrc(v, j) : rv;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
-      dma16_asm(r, lds0 + 2 * C::TILE + buf * C::TILE + (i * NW + wave) * 1024, voff0, toff + i * SEG_ROW_STEP * rsb);
+#pragma unroll
+      for (int s2 = 0; s2 < NSETS; ++s2)
+        dma16_asm(r, lds0 + 2 * C::TILE + buf * C::TILE + (i * NW + (LOADER ? s2 : wave)) * 1024, voff[s2],
+                  toff + i * SEG_ROW_STEP * rsb);
   };
 
   // ---- per-lane LDS read offsets
@@ -504,8 +525,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     constexpr int NSEG = D * D * 2 / 1024;  // 1 KB fragments
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(sfrag + (size_t)(b * H + h) * stride_bh + (size_t)n * stride_frame, D * D * 2);
+    if (!is_loader) {
 #pragma unroll
-    for (int i = wave; i < NSEG; i += NW) dma16_to_lds(rs, smem + i * 1024, lane * 16, i * 1024);
+      for (int i = wave; i < NSEG; i += NW) dma16_to_lds(rs, smem + i * 1024, lane * 16, i * 1024);
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
@@ -531,15 +554,17 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(
     const float* Sp = states + (long long)(b * H + h) * stride_bh + (long long)n * stride_frame;
     constexpr int NPER = D * D / 4 / NT;  // 16-byte pieces of S per thread
     static_assert(NPER * NT * 4 == D * D, "S must split evenly over the threads");
-    f32x4 sx[NPER];
+    if (!is_loader) {  // the NT threads of the compute waves
+      f32x4 sx[NPER];
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) sx[i] = *reinterpret_cast<const f32x4*>(Sp + (tid + i * NT) * 4);
+      for (int i = 0; i < NPER; ++i) sx[i] = *reinterpret_cast<const f32x4*>(Sp + (tid + i * NT) * 4);
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int p = tid + i * NT;
-      const int dk = p / (D / 4), dv0 = (p % (D / 4)) * 4;
-      const int off = dk * (D * 2) + (((dv0 >> 3) ^ v_swz<NCH>(dk)) << 4) + (dv0 & 7) * 2;
-      *reinterpret_cast<u32x2*>(smem + off) = u32x2{pack_bf16x2(sx[i][0], sx[i][1]), pack_bf16x2(sx[i][2], sx[i][3])};
+      for (int i = 0; i < NPER; ++i) {
+        const int p = tid + i * NT;
+        const int dk = p / (D / 4), dv0 = (p % (D / 4)) * 4;
+        const int off = dk * (D * 2) + (((dv0 >> 3) ^ v_swz<NCH>(dk)) << 4) + (dv0 & 7) * 2;
+        *reinterpret_cast<u32x2*>(smem + off) = u32x2{pack_bf16x2(sx[i][0], sx[i][1]), pack_bf16x2(sx[i][2], sx[i][3])};
+      }
     }
     __syncthreads();
     if (!wave_active) return;
@@ -638,22 +663,26 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
   const long long items = (long long)s.B * s.H * s.F * qtiles;
   const int grid = (int)((items + 7) / 8 * 8);
   const float c2 = scale * kLog2e;
+  // at most one work-group per CU: a loader wave issues the tile copies
+  const bool loader = items <= kLoaderMaxGroups;
+  const int nt = loader ? NT + kWave : NT;
   HA_LOG("launch attn_bf16_kernel<%d>: grid %d x %d threads (%lld items = %d streams x %d heads x %d frames x %d "
-         "query tiles of %d; key tiles of %d, %d KiB LDS; readout from %s%s)",
-         s.d, grid, NT, items, s.B, s.H, s.F, qtiles, QPB, KT, (s.d == 128 ? Cfg<128>::SMEM : Cfg<64>::SMEM) >> 10,
-         sfrag ? "bf16 fragments" : "fp32 states", mix ? "; per-branch weights" : "");
+         "query tiles of %d; key tiles of %d, %d KiB LDS; readout from %s%s%s)",
+         s.d, grid, nt, items, s.B, s.H, s.F, qtiles, QPB, KT, (s.d == 128 ? Cfg<128>::SMEM : Cfg<64>::SMEM) >> 10,
+         sfrag ? "bf16 fragments" : "fp32 states", mix ? "; per-branch weights" : "",
+         loader ? "; a loader wave issues the tile copies" : "");
   auto args = [&](auto kern) {
-    kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+    kern<<<grid, nt, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                               (const uint16_t*)qp, states, stride_bh, stride_frame,
                               (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
                               qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr, mix);
   };
   if (mix) {
-    if (s.d == 128) args(attn_bf16_kernel<128, false, true>);
-    else args(attn_bf16_kernel<64, false, true>);
+    if (s.d == 128) loader ? args(attn_bf16_kernel<128, false, true, true>) : args(attn_bf16_kernel<128, false, true>);
+    else loader ? args(attn_bf16_kernel<64, false, true, true>) : args(attn_bf16_kernel<64, false, true>);
   } else {
-    if (s.d == 128) args(attn_bf16_kernel<128, false>);
-    else args(attn_bf16_kernel<64, false>);
+    if (s.d == 128) loader ? args(attn_bf16_kernel<128, false, false, true>) : args(attn_bf16_kernel<128, false>);
+    else loader ? args(attn_bf16_kernel<64, false, false, true>) : args(attn_bf16_kernel<64, false>);
   }
   return hipGetLastError();
 }
