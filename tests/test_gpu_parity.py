@@ -526,3 +526,69 @@ def test_graph_replay_matches_eager(L):
         junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
+
+
+# --- the forward call's scan inside the attention launch -----------------------
+# (calls over several frames with more than 256 attention work-groups: the
+# scan's work-groups publish each frame's state as readout fragments and the
+# attention work-groups wait for them; the same operations as the separate
+# state update and readout, so the results must be bitwise equal)
+
+@pytest.mark.parametrize("d,H,L,F", [(128, 8, 200, 17), (128, 4, 300, 24), (64, 8, 129, 17), (128, 12, 1560, 3)])
+def test_fused_scan_matches_sub_entry_points(d, H, L, F):
+    w = small("480p", B=1, H=H, d=d, L=L, frames=F, state0_sigma=0.05)
+    assert w.B * w.H * w.frames * ((L + 127) // 128) > 256
+    say(f"case fused scan d={d} H={H} L={L} F={F}")
+    inp = W.make_call_inputs(w, 0, F, 0)
+    dev = upload(inp, "bf16")
+    s0 = torch.from_numpy(W.make_state0(w)).cuda()
+    st = s0.clone()
+    out = run_gpu(dev, st, w.L, True)
+    st2 = s0.clone()
+    snaps = torch.empty(1, H, F, d, d, device="cuda")
+    api.hybrid_attn_state_update(dev["kp"], dev["vp"], dev["alpha"], dev["beta"], st2, w.L, snapshots=snaps)
+    out2 = api.hybrid_attn_intra_readout(dev["q"], dev["k"], dev["v"], dev["qp"], snaps, F * d * d, d * d, w.L)
+    torch.cuda.synchronize()
+    assert torch.equal(st, st2)
+    assert torch.equal(out, out2)
+
+
+def test_fused_scan_graph_replay_matches_eager():
+    # the frame counters are zeroed by each call's gram kernel, so replays of
+    # a captured call start clean
+    w = small("480p", B=1, H=8, L=200, frames=17, state0_sigma=0.05)
+    say("case fused scan, graph replay")
+    dev = upload(W.make_call_inputs(w, 0, w.frames, 0), "bf16")
+    s0 = torch.from_numpy(W.make_state0(w)).cuda()
+    out = torch.empty_like(dev["q"])
+    ws = torch.empty(api.workspace_bytes(1, w.H, w.T, w.L, w.d, 1), dtype=torch.uint8, device="cuda")
+
+    def call(state):
+        api.hybrid_attn_forward(dev["q"], dev["k"], dev["v"], dev["qp"], dev["kp"], dev["vp"], dev["alpha"],
+                                dev["beta"], state, w.L, 1, out=out, workspace=ws)
+
+    st = s0.clone()
+    ref = []
+    for _ in range(3):
+        call(st)
+        torch.cuda.synchronize()
+        ref.append((out.clone(), st.clone()))
+    gst = s0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(gst)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(gst)
+    torch.cuda.synchronize()
+    gst.copy_(s0)
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[i][0]) and torch.equal(gst, ref[i][1])
+        junk = torch.randn(1 << 16, device="cuda").sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)

@@ -46,6 +46,13 @@
 // takes 64 bytes per clock). A fifth wave then issues every copy and the four
 // compute waves only compute; the step barrier still orders the buffers.
 //
+// Fused scan (FUSED, forward calls over several frames): the first
+// work-groups of the launch run the clean pass's state scan (scan_role below)
+// and publish S_{n-1} of every frame as readout fragments; an attention
+// work-group of frame n waits at its readout until all column blocks of its
+// frame's state are published, so the scan runs beside the attention instead
+// of before it.
+//
 // KV mode (the softmax teacher with a full KV cache that the hybrid layer
 // replaces, ARL2 section 1): the same kernel with frame n's queries attending
 // to the keys [0, kv_off + (n+1) L) of a key/value cache, no readout. The keys
@@ -69,7 +76,6 @@ constexpr int NW = 4;           // waves per work-group
 constexpr int QPB = QPW * NW;   // queries per work-group
 constexpr int NT = NW * kWave;  // threads per work-group
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kLoaderMaxGroups = 256;  // launches up to this many work-groups take the loader wave
 
 template <int D>
 struct Cfg {
@@ -114,13 +120,133 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+constexpr int kDevice = 16;              // cache policy: sc1 (device scope)
+constexpr int kSpinLimit = 1 << 22;      // polls of a frame counter (a guard: it cannot run out)
+
+// The clean pass's state scan as work-group (bh, cb) of the fused launch:
+// column block cb of the state of (stream, head) bh walks the frames in order,
+// S_n = alpha_n S_{n-1} + (-G_n) S_{n-1} + B_n with the increments ws of the
+// gram kernel, on MFMA with -G and S split into bf16 hi + lo (the product of
+// state_scan_mfma_kernel, the same operations in the same order, so the same
+// result). Wave w < d/32 keeps rows [32w, 32w+32) of the block in its
+// accumulator and loads its band's -G fragments of the next frame into
+// registers; the S exchange goes through LDS. Each S_{n-1} is stored as the
+// readout fragments of frame n with device-scope stores; after the next
+// barrier (each wave's stores acknowledged before it) one lane adds one to
+// flags[bh*F + n]. The last state goes to state (fp32).
+template <int D>
+__device__ __forceinline__ void scan_role(const unsigned char* __restrict__ ws, const float* __restrict__ alpha,
+                                          float* __restrict__ state, unsigned char* __restrict__ sfrag,
+                                          unsigned* __restrict__ flags, int bh, int cb, int H, int F,
+                                          unsigned char* smem, int wave, int lane) {
+  constexpr int NRB = D / 32, NCB = D / 32, KS = D / 16;
+  constexpr size_t PER = (size_t)D * D * 8;  // increment bytes per (b, h, frame)
+  u32x4(*lds)[2][KS][64] = reinterpret_cast<u32x4(*)[2][KS][64]>(smem);  // [slot][hi, lo][k-step][lane]
+  static_assert(2 * 2 * KS * 64 * 16 <= 4 * KT * D * 2, "the exchange must fit in the tile buffers");
+  const bool comp = wave < NRB;
+  const int w = comp ? wave : 0;
+  const int lr = lane & 31, hh = lane >> 5;
+  const int row0 = w * 32, col = cb * 32 + lr;
+  const int b = bh / H, h = bh % H;
+  f32x16 acc = f32x16{};
+  float* sbase = state + (size_t)bh * D * D;
+  if (comp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col];
+  }
+  u32x4 gh[KS], gl[KS];
+  f32x4 bv[2][4];
+  float al[2] = {0.f, 0.f};
+  auto fetch_g = [&](int n) {
+    const u32x4* gp = reinterpret_cast<const u32x4*>(ws + ((size_t)bh * F + n) * PER);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      gh[ks] = gp[(w * KS + ks) * 64 + lane];
+      gl[ks] = gp[(NRB * KS + w * KS + ks) * 64 + lane];
+    }
+  };
+  auto fetch_b = [&](int slot, int n) {
+    const unsigned char* base = ws + ((size_t)bh * F + n) * PER;
+    const f32x4* bp = reinterpret_cast<const f32x4*>(base + (size_t)D * D * 4) + ((size_t)(cb * NRB + w) * 64 + lane) * 4;
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) bv[slot][v4] = bp[v4];
+    al[slot] = alpha[((size_t)b * F + n) * H + h];
+  };
+  const __amdgpu_buffer_rsrc_t rsf = make_rsrc(sfrag + (size_t)bh * F * D * D * 2, F * D * D * 2);
+  // S_{n-1} (acc) -> exchange slot SL as B fragments (k-steps 2w, 2w+1: registers
+  // [8s, 8s+8)) and, its hi part, the readout fragments of frame n
+  auto publish = [&](auto slot_c, int n) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float x0 = acc[8 * sh + 2 * w2], x1 = acc[8 * sh + 2 * w2 + 1];
+        const uint32_t hp = pack_bf16x2(x0, x1);
+        hi[w2] = hp;
+        lo[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hp), x1 - bf16_hi_to_f32(hp));
+      }
+      lds[SL][0][2 * w + sh][lane] = hi;
+      lds[SL][1][2 * w + sh][lane] = lo;
+      __builtin_amdgcn_raw_buffer_store_b128(hi, rsf, (uint32_t)((((n * NCB + cb) * KS) + 2 * w + sh) * 64 + lane) * 16, 0,
+                                             kDevice);
+    }
+  };
+  if (comp) {
+    fetch_g(0);
+    fetch_b(0, 0);
+    if (F > 1) fetch_b(1, 1);
+    publish(std::integral_constant<int, 0>{}, 0);
+  }
+  auto step = [&](auto slot_c, int n) {
+    constexpr int SL = decltype(slot_c)::value;
+    // every wave's fragments of frame n are stored (acknowledged) and its S
+    // exchange is in LDS
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (wave == 0 && lane == 0) __hip_atomic_fetch_add(flags + (size_t)bh * F + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (comp) {
+      f32x16 nacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nacc[r] = fmaf(al[SL], acc[r], bv[SL][r >> 2][r & 3]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 shi = lds[SL][0][ks][lane];
+        const u32x4 slo = lds[SL][1][ks][lane];
+        nacc = mfma32x32x16(gh[ks], shi, nacc);
+        nacc = mfma32x32x16(gh[ks], slo, nacc);
+        nacc = mfma32x32x16(gl[ks], shi, nacc);
+      }
+      if (n + 1 < F) fetch_g(n + 1);
+      if (n + 2 < F) fetch_b(SL, n + 2);
+      acc = nacc;
+      if (n + 1 < F) publish(std::integral_constant<int, SL ^ 1>{}, n + 1);
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int n = 0;
+  for (; n + 1 < F; n += 2) {
+    step(S0{}, n);
+    step(S1{}, n + 1);
+  }
+  if (n < F) step(S0{}, n);
+  if (comp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
+  }
+}
+
 template <int P_, bool NEXT_, bool TAIL_, bool LOADK_>
 struct StepFlags {
   static constexpr int P = P_;
   static constexpr bool NEXT = NEXT_, TAIL = TAIL_, LOADK = LOADK_;
 };
 
-template <int D, bool KV, bool MIX = false, bool LOADER = false>
+template <int D, bool KV, bool MIX = false, bool LOADER = false, bool FUSED = false>
 __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ qp,
@@ -128,7 +254,8 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
     const unsigned char* __restrict__ sfrag, uint16_t* __restrict__ out, int H, int T, int L, int F,
     int qtiles, int n_items, float c2 /* softmax scale * log2(e) */,
     int Tk, int kv_off, int nsplit, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    const float* __restrict__ add_o, const float* __restrict__ mix) {
+    const float* __restrict__ add_o, const float* __restrict__ mix, const unsigned char* __restrict__ gws,
+    const float* __restrict__ alpha, float* __restrict__ state, unsigned* __restrict__ flags, int n_scan) {
   using C = Cfg<D>;
   constexpr int NCH = C::NCH;
   __shared__ __align__(16) unsigned char smem[C::SMEM];
@@ -150,7 +277,25 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
     b = bh / H;
     h = bh % H;
   } else {
-    const int item = xcd_major_item(gridDim.x);
+    int item;
+    if constexpr (FUSED) {
+      const int g = blockIdx.x;
+      if (g < n_scan) {
+        // the scan's work-groups come first (they hold CU slots before any
+        // attention work-group can wait for them), XCD-major with the column
+        // blocks of one (b, h) on one XCD
+        constexpr int NCB = D / 32;
+        const int si = (g & 7) * (n_scan >> 3) + (g >> 3);
+        if (si >= n_items / (F * qtiles) * NCB) return;
+        scan_role<D>(gws, alpha, state, const_cast<unsigned char*>(sfrag), flags, si / NCB, si % NCB, H, F, smem,
+                     __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), (int)threadIdx.x & 63);
+        return;
+      }
+      const int ga = g - n_scan;
+      item = (ga & 7) * ((int)(gridDim.x - n_scan) >> 3) + (ga >> 3);
+    } else {
+      item = xcd_major_item(gridDim.x);
+    }
     if (item >= n_items) return;
     qt = item % qtiles;
     const int hf = item / qtiles;
@@ -164,6 +309,7 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int lr = lane & 31, hh = lane >> 5;
   static_assert(!(KV && LOADER), "the loader wave serves the readout kernel only");
+  static_assert(!FUSED || (!KV && !LOADER && !MIX), "the fused scan serves the plain forward call only");
   const bool is_loader = LOADER && wave == NW;
   // debug bit 1: the work item decodes to a valid (b, h, frame, query tile, split)
   HA_CHECK(qt >= 0 && qt < qtiles && h >= 0 && h < H && n >= 0 && n < F && b >= 0 && sp >= 0 && sp < nsplit, 1);
@@ -525,9 +671,21 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
     constexpr int NSEG = D * D * 2 / 1024;  // 1 KB fragments
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(sfrag + (size_t)(b * H + h) * stride_bh + (size_t)n * stride_frame, D * D * 2);
+    if constexpr (FUSED) {
+      // the frame's state: all column blocks published by the scan work-groups
+      if (wave == 0 && lane == 0) {
+        const unsigned* fl = flags + ((size_t)(b * H + h) * F + n);
+        int it = 0;
+        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)(D / 32) &&
+               ++it < kSpinLimit)
+          __builtin_amdgcn_s_sleep(2);
+        HA_CHECK(it < kSpinLimit, 16);  // debug bit 16: a frame counter never completed
+      }
+      __syncthreads();
+    }
     if (!is_loader) {
 #pragma unroll
-      for (int i = wave; i < NSEG; i += NW) dma16_to_lds(rs, smem + i * 1024, lane * 16, i * 1024);
+      for (int i = wave; i < NSEG; i += NW) dma16_to_lds<FUSED ? kDevice : 0>(rs, smem + i * 1024, lane * 16, i * 1024);
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
@@ -664,7 +822,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
   const int grid = (int)((items + 7) / 8 * 8);
   const float c2 = scale * kLog2e;
   // at most one work-group per CU: a loader wave issues the tile copies
-  const bool loader = items <= kLoaderMaxGroups;
+  const bool loader = items <= kAttnLoaderMaxGroups;
   const int nt = loader ? NT + kWave : NT;
   HA_LOG("launch attn_bf16_kernel<%d>: grid %d x %d threads (%lld items = %d streams x %d heads x %d frames x %d "
          "query tiles of %d; key tiles of %d, %d KiB LDS; readout from %s%s%s)",
@@ -675,7 +833,8 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
     kern<<<grid, nt, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                               (const uint16_t*)qp, states, stride_bh, stride_frame,
                               (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
-                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr, mix);
+                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr, mix, nullptr, nullptr,
+                              nullptr, nullptr, 0);
   };
   if (mix) {
     if (s.d == 128) loader ? args(attn_bf16_kernel<128, false, true, true>) : args(attn_bf16_kernel<128, false, true>);
@@ -684,6 +843,32 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
     if (s.d == 128) loader ? args(attn_bf16_kernel<128, false, false, true>) : args(attn_bf16_kernel<128, false>);
     else loader ? args(attn_bf16_kernel<64, false, false, true>) : args(attn_bf16_kernel<64, false>);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_scan_bf16(const void* q, const void* k, const void* v, const void* qp, const void* ws,
+                                 const float* alpha, float* state, void* sfrag, unsigned* flags, void* out,
+                                 const Shape& s, float scale, hipStream_t st) {
+  const int qtiles = (s.L + QPB - 1) / QPB;
+  const long long items = (long long)s.B * s.H * s.F * qtiles;
+  const int ncb = s.d / 32;
+  const int units = s.B * s.H * ncb;
+  const int n_scan = 8 * ((units + 8 * ncb - 1) / (8 * ncb) * ncb);  // whole (b, h) units per XCD
+  const int grid = n_scan + (int)((items + 7) / 8 * 8);
+  const float c2 = scale * kLog2e;
+  const long long fb = (long long)s.d * s.d * 2;  // fragment bytes per frame
+  HA_LOG("launch attn_bf16_kernel<%d> with the state scan: grid %d x %d threads (%d scan work-groups for %d (b, h, "
+         "column block) units walking %d frames, then %lld attention items = %d streams x %d heads x %d frames x %d "
+         "query tiles; each waits for its frame's state)",
+         s.d, grid, NT, n_scan, units, s.F, items, s.B, s.H, s.F, qtiles);
+  auto args = [&](auto kern) {
+    kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)qp,
+                              nullptr, s.F * fb, fb, (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
+                              qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr, nullptr,
+                              (const unsigned char*)ws, alpha, state, flags, n_scan);
+  };
+  if (s.d == 128) args(attn_bf16_kernel<128, false, false, false, true>);
+  else args(attn_bf16_kernel<64, false, false, false, true>);
   return hipGetLastError();
 }
 
@@ -711,7 +896,8 @@ hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
                               nullptr, 0, 0, nullptr, (uint16_t*)out, s.H, s.T, s.L, s.F, qtiles, units, c2, Tk,
-                              kv_off, nsplit, part_o, (float2*)part_ml, add_o, nullptr);
+                              kv_off, nsplit, part_o, (float2*)part_ml, add_o, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              0);
   };
   if (s.d == 128) args(attn_bf16_kernel<128, true>);
   else args(attn_bf16_kernel<64, true>);

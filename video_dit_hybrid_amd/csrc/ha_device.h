@@ -82,9 +82,11 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const unsigned char* p) {
 // voff + soff; out-of-range lanes write zeros. The builtin is only compiled in
 // the device pass: clang's host pass drops the host handle of a kernel
 // template whose body names it.
+// AUX: the cache policy bits (16: sc1, device scope).
+template <int AUX = 0>
 __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(lds), 16, voff, soff, 0, AUX);
 #endif
 }
 __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {

@@ -18,10 +18,26 @@ struct Shape {
 // n*stride_frame, the two strides then counted in bytes.
 // mix, if not null: fp32 [B, H, 2] weights (w_softmax, w_inter) per (stream,
 // head); the output is then w_softmax O/l + w_inter Q'S instead of the sum.
+// Attention work-groups of a call: one per (stream, head, frame, 128-query
+// tile). Launches of at most kAttnLoaderMaxGroups (one per CU) take the
+// kernel with a loader wave; larger ones the kernel without it, and of those
+// the forward call over several frames runs its state scan in the same launch.
+constexpr int kAttnLoaderMaxGroups = 256;
+inline long long attn_groups(const Shape& s) { return (long long)s.B * s.H * s.F * ((s.L + 127) / 128); }
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const void* qp,
                             const float* states, long long stride_bh, long long stride_frame,
                             const void* sfrag, void* out, const Shape& s, float scale,
                             hipStream_t st, const float* mix = nullptr);
+// The forward call's state scan and its attention in one launch (bf16, F > 1):
+// the first work-groups walk the frames as state_scan_mfma_kernel does (from
+// the increments ws written by launch_gram_bf16, advancing state to S_F),
+// publishing each S_{n-1} as readout fragments to sfrag (strides F*d*d*2 and
+// d*d*2 bytes) and counting each frame's published column blocks in
+// flags[(b*H + h)*F + n], which launch_gram_bf16 zeroed; the attention
+// work-groups of frame n wait for that count before their readout.
+hipError_t launch_attn_scan_bf16(const void* q, const void* k, const void* v, const void* qp, const void* ws,
+                                 const float* alpha, float* state, void* sfrag, unsigned* flags, void* out,
+                                 const Shape& s, float scale, hipStream_t st);
 
 // KV mode of the same kernel (the softmax teacher with a full KV cache): the
 // queries of call frame n (q, out [B, T, H, d], T = F * L) attend to the keys
@@ -56,8 +72,10 @@ hipError_t launch_attn_fp32(const void* q, const void* k, const void* v, const v
 
 // Per-frame increments G_n = K'^T diag(beta) K', B_n = K'^T diag(beta) V'.
 // bf16 path workspace, per (b, h, frame): [-G hi bf16 d x d][-G lo bf16 d x d][B fp32 d x d].
+// flags, if not null: B*H*F words set to zero (the counters of
+// launch_attn_scan_bf16).
 hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, float* gram,
-                            const Shape& s, hipStream_t st);
+                            const Shape& s, hipStream_t st, unsigned* flags = nullptr);
 // fp32 path workspace, per (b, h, frame): [G | B] fp32 d x 2d.
 // The same pass writing only fp32 partial sums (partial_block layout of
 // ha_gram_format.h), nsplit token splits per (b, h, frame). With beta2 not

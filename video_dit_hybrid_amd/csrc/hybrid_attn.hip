@@ -236,6 +236,17 @@ ha_status launch_forward(const ForwardArgs& a, const ha::Shape& s, void* workspa
     return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
   }
   void* snap_area = (char*)workspace + align_up(ha::update_bytes(s));
+  if (a.dtype == HA_BF16 && !a.mix && ha::attn_groups(s) > ha::kAttnLoaderMaxGroups) {
+    // the scan runs in the attention launch: its work-groups publish each
+    // frame's S_{n-1} as readout fragments and count them per frame (the
+    // counters follow the fragments in the snapshot area, which is sized for
+    // fp32 snapshots; the gram kernel zeroes them)
+    unsigned* flags = (unsigned*)((char*)snap_area + align_up(ha::snapshot_frag_bytes(s)));
+    if (ha::launch_gram_bf16(a.kp, a.vp, a.beta, gram, s, st, flags) != hipSuccess) return HA_ERR_DEVICE;
+    const ha_status r = launched(ha::launch_attn_scan_bf16(a.q, a.k, a.v, a.qp, gram, a.alpha, a.state, snap_area,
+                                                           flags, a.out, s, scale, st));
+    return r != HA_OK ? r : check_finite("state", a.state, nstate, st);
+  }
   if (a.dtype == HA_BF16) {
     // S_{n-1} of every frame as bf16 readout fragments (the readout rounds the
     // state to bf16 either way)

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
                                                        const float* __restrict__ beta2,
                                                        float* __restrict__ gram,
                                                        float* __restrict__ partial, int nsplit,
-                                                       int H, int T, int L, int F) {
+                                                       int H, int T, int L, int F, unsigned* __restrict__ flags) {
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
   constexpr int TILE = TC * D * 2;           // bytes of one K' or V' chunk
   constexpr int BUF = 2 * TILE + TC * 4 * (TWO ? 2 : 1);  // K', V', beta (and beta2)
@@ -94,6 +94,8 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
   const int kh = NRB == 4 ? ((wave >> 1) & 1) : (wave & 3);
   // only the upper-triangle G blocks, when writing the scan's format
   const bool tri = !TWO && partial == nullptr;
+  // the frame's counter of the fused scan and attention starts at zero
+  if (flags && sp == 0 && tid == 0) flags[((size_t)b * H + h) * F + n] = 0u;
 
   const uint32_t rsb = (uint32_t)H * D * 2;
   const long long fbase = ((long long)b * T + (long long)n * L) * ((long long)H * D) + (long long)h * D;
@@ -372,7 +374,7 @@ hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float
          NT, nsplit, beta2 ? ", two step-size vectors" : "");
   auto run = [&](auto gk) {
     gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, beta2, nullptr, partial, nsplit, s.H,
-                            s.T, s.L, s.F);
+                            s.T, s.L, s.F, nullptr);
   };
   if (s.d == 128) {
     if (beta2) run(gram_bf16_kernel<128, true>);
@@ -385,7 +387,7 @@ hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float
 }
 
 hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, float* gram,
-                            const Shape& s, hipStream_t st) {
+                            const Shape& s, hipStream_t st, unsigned* flags) {
   const long long groups = (long long)s.B * s.H * s.F;
   const int nsplit = gram_splits(s);
   // partial sums after the increments (gram_bytes reserves both)
@@ -395,7 +397,7 @@ hipError_t launch_gram_bf16(const void* kp, const void* vp, const float* beta, f
          groups, nsplit, nsplit > 1 ? " + gram_reduce_kernel" : "");
   auto run = [&](auto gk, auto rk, int nrb) {
     gk<<<grid, NT, 0, st>>>((const uint16_t*)kp, (const uint16_t*)vp, beta, nullptr, gram, partial, nsplit,
-                            s.H, s.T, s.L, s.F);
+                            s.H, s.T, s.L, s.F, flags);
     if (nsplit > 1) rk<<<(int)(groups * nrb * nrb), 256, 0, st>>>(partial, gram, nsplit, s.H, s.F);
   };
   if (s.d == 128) run(gram_bf16_kernel<128, false>, gram_reduce_kernel<128>, 4);
