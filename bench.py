@@ -1,6 +1,6 @@
 """Throughput of the hybrid attention layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 480p] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--workload 480p] [--no-cpu]
 
 Variants (not the headline line): --variant fmap (per-head feature maps
 applied inside the call) and --variant gated (gates projected from the layer
@@ -20,7 +20,11 @@ denoise calls + 1 clean call, F=1 per call; frames/s over all 600 calls);
 
 A step is one clean-pass layer call over the whole workload: intra-frame
 softmax + Q'S readout for every frame and the per-frame state write (all
-inputs already resident in HBM). Default workload: the Wan-1.3B-shaped 480p
+inputs already resident in HBM). The warmup is long enough for the core
+clock to ramp up: from idle the chip runs the first ~10 ms of calls about
+15 % slower than from then on (measured over 300 consecutive 480p calls:
+0.50 ms per call in the first 20, 0.42-0.43 ms in every later batch of 20,
+and 0.51 ms again after one second idle). Default workload: the Wan-1.3B-shaped 480p
 layer, B=1, H=12, d=128, 21 frames x 1560 tokens, bf16 inputs, fp32 state.
 
 Prints one JSON line. `value` is frames/s of the whole layer call; `roofline`
@@ -713,8 +717,8 @@ def bench_token_level(w, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "tiny", "stream", "batched"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
