@@ -387,7 +387,7 @@ def attention_roofline(w, t, steps):
     return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_for_current_kernel() if w.name == "480p" else None,
-            "kernel": "attn_bf16_kernel<128, false, false, false> (intra-frame softmax + readout)", "avg_launch_ms": round(ms, 4)}
+            "kernel": "attn_bf16_kernel<128, false, false, false, false> (intra-frame softmax + readout)", "avg_launch_ms": round(ms, 4)}
 
 
 def cpu_model():
@@ -536,7 +536,7 @@ def bench_kvcache(args):
            "kv_cache_ms_per_frame": {str(n): round(t, 4) for n, t in t_kv.items()},
            "roofline": {"bound": "mfma", "achieved": round(tf_last, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf_last / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                        "kernel": f"attn_bf16_kernel<128, true, false, false> over {n_last + 1} frames of keys (whole passes: "
+                        "kernel": f"attn_bf16_kernel<128, true, false, false, false> over {n_last + 1} frames of keys (whole passes: "
                                   "cache append, attention, split merge)",
                         "flop_per_frame": flop_last, "avg_frame_ms": round(t_kv[n_last], 4)},
            "video_curve": curve}
@@ -891,7 +891,7 @@ def main():
     traffic = traffic_for_current_kernel() if w.name == "480p" else None
     roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "kernel": "attn_bf16_kernel<128, false, false, false> (intra-frame softmax + Q'S readout)",
+            "kernel": "attn_bf16_kernel<128, false, false, false, false> (intra-frame softmax + Q'S readout)",
             "flop_per_launch": att + rd, "avg_launch_ms": round(attn_ms, 4),
             "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4), "min_launch_ms": round(launch_ms[0], 4)}
     # The core clock under this kernel is well below the 2.4 GHz the peak
