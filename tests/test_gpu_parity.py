@@ -534,18 +534,19 @@ def test_graph_replay_matches_eager(L):
 # attention work-groups wait for them; the same operations as the separate
 # state update and readout, so the results must be bitwise equal)
 
-@pytest.mark.parametrize("d,H,L,F", [(128, 8, 200, 17), (128, 4, 300, 24), (64, 8, 129, 17), (128, 12, 1560, 3)])
-def test_fused_scan_matches_sub_entry_points(d, H, L, F):
-    w = small("480p", B=1, H=H, d=d, L=L, frames=F, state0_sigma=0.05)
+@pytest.mark.parametrize("d,B,H,L,F", [(128, 1, 8, 200, 17), (128, 1, 4, 300, 24), (64, 1, 8, 129, 17),
+                                       (128, 1, 12, 1560, 3), (128, 2, 4, 200, 17)])
+def test_fused_scan_matches_sub_entry_points(d, B, H, L, F):
+    w = small("480p", B=B, H=H, d=d, L=L, frames=F, state0_sigma=0.05)
     assert w.B * w.H * w.frames * ((L + 127) // 128) > 256
-    say(f"case fused scan d={d} H={H} L={L} F={F}")
+    say(f"case fused scan d={d} B={B} H={H} L={L} F={F}")
     inp = W.make_call_inputs(w, 0, F, 0)
     dev = upload(inp, "bf16")
     s0 = torch.from_numpy(W.make_state0(w)).cuda()
     st = s0.clone()
     out = run_gpu(dev, st, w.L, True)
     st2 = s0.clone()
-    snaps = torch.empty(1, H, F, d, d, device="cuda")
+    snaps = torch.empty(B, H, F, d, d, device="cuda")
     api.hybrid_attn_state_update(dev["kp"], dev["vp"], dev["alpha"], dev["beta"], st2, w.L, snapshots=snaps)
     out2 = api.hybrid_attn_intra_readout(dev["q"], dev["k"], dev["v"], dev["qp"], snaps, F * d * d, d * d, w.L)
     torch.cuda.synchronize()
