@@ -5,13 +5,17 @@
 // Launch order of a call (ARL2 section 2.2: every token of frame N reads
 // S_{N-1}; the state is written once per clean frame, after the frame):
 //   update_state = 0      : readout kernel on `state` for every frame.
-//   update_state = 1, F=1 : readout on `state`, then gram, then the scan
-//                           writes S_1 into `state` (same stream, so the
-//                           readout has read S_0 before it is overwritten).
+//   update_state = 1, F=1 : readout on `state`, then the state write into
+//                           `state` (one kernel at d = 128 in bf16, else gram
+//                           and scan; same stream, so the readout has read
+//                           S_0 before it is overwritten).
 //   update_state = 1, F>1 : gram, scan (writes S_{n-1} snapshots to the
 //                           workspace and S_F to `state`), then the readout
 //                           on the snapshots (bf16 readout fragments on the
-//                           bf16 path, fp32 row-major on the fp32 path).
+//                           bf16 path, fp32 row-major on the fp32 path). In
+//                           bf16 with more than 256 attention work-groups the
+//                           scan runs as the first work-groups of the readout's
+//                           launch, which wait frame by frame for it.
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
