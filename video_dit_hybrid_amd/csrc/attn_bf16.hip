@@ -585,8 +585,15 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
   }
   // Remaining 1 to 3 tiles, without the software pipeline (one score tile
   // live): S_t is in sa, V_t in buffer t % 2, K_{t+1} in buffer (t+1) % 2.
+  // FUSED: the frame's counter (below) is first read during the last tile,
+  // so that the device-scope load's latency hides behind the tile's work
+  unsigned fl_seen = 0;
   for (int t = j; t < ntiles; ++t) {
     const int pb = t & 1;
+    if constexpr (FUSED) {
+      if (t + 1 == ntiles && wave == 0 && lane == 0)
+        fl_seen = __hip_atomic_load(flags + ((size_t)(b * H + h) * F + n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (t + 1 < ntiles) issue_v(t + 1, pb ^ 1);
     if (t + 2 < ntiles) issue_k(t + 2, pb);
     if (wave_active) {
@@ -601,7 +608,13 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
       }
     }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (FUSED) {
+      // the last tile copies nothing: wait for LDS only, the counter load may stay in flight
+      if (t + 1 == ntiles) __builtin_amdgcn_s_waitcnt(0xC07F);
+      else __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
@@ -675,10 +688,12 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
       // the frame's state: all column blocks published by the scan work-groups
       if (wave == 0 && lane == 0) {
         const unsigned* fl = flags + ((size_t)(b * H + h) * F + n);
+        unsigned seen = fl_seen;
         int it = 0;
-        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)(D / 32) &&
-               ++it < kSpinLimit)
+        while (seen < (unsigned)(D / 32) && ++it < kSpinLimit) {
           __builtin_amdgcn_s_sleep(2);
+          seen = __hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         HA_CHECK(it < kSpinLimit, 16);  // debug bit 16: a frame counter never completed
       }
       __syncthreads();
