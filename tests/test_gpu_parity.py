@@ -535,7 +535,8 @@ def test_graph_replay_matches_eager(L):
 # state update and readout, so the results must be bitwise equal)
 
 @pytest.mark.parametrize("d,B,H,L,F", [(128, 1, 8, 200, 17), (128, 1, 4, 300, 24), (64, 1, 8, 129, 17),
-                                       (128, 1, 12, 1560, 3), (128, 2, 4, 200, 17)])
+                                       (128, 1, 12, 1560, 3), (128, 2, 4, 200, 17), (128, 1, 12, 1560, 2),
+                                       (128, 1, 8, 24, 40)])
 def test_fused_scan_matches_sub_entry_points(d, B, H, L, F):
     w = small("480p", B=B, H=H, d=d, L=L, frames=F, state0_sigma=0.05)
     assert w.B * w.H * w.frames * ((L + 127) // 128) > 256
