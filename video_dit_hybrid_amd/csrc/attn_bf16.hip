@@ -339,8 +339,12 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
     return rsrc_words(base + kvbase + (long long)(t0 + j) * KT * H * D, (int)((uint32_t)(rows - 1) * rsb + D * 2));
   };
 
-  const int q0 = qt * QPB + (is_loader ? 0 : wave) * QPW;
-  const bool wave_active = !is_loader && q0 < L;
+  // a frame's last query tile holding at most one wave's queries (1560 =
+  // 12 x 128 + 24): waves 0 and 1 both take its queries, each with one 32-key
+  // half of every key tile (tsplit below), instead of one wave with all keys
+  const bool tsplit = !KV && L - qt * QPB <= QPW;
+  const int q0 = qt * QPB + ((is_loader || tsplit) ? 0 : wave) * QPW;
+  bool wave_active = !is_loader && (tsplit ? wave < 2 : q0 < L);
   const int my_q = q0 + lr;
 
   // ---- direct-to-LDS tile loads. Load i of wave w fills the 1 KB LDS segment
@@ -521,102 +525,202 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
     }
   };
 
-  // ---- prologue: K_0, V_0, K_1 in flight, then S_0
-  issue_k(0, 0);
-  issue_v(0, 0);
-  if (ntiles > 1) issue_k(1, 1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x16 sa0, sa1, sb0, sb1;
-  float mt_a = 0.f, mt_b = 0.f;
-  if (wave_active) {
-    qk(kbuf, sa0, sa1);
-    if (ntiles == 1 && last_valid < KT) mask_tail(sa0, sa1);
-    mt_a = tile_max(sa0, sa1);
-  }
-  __syncthreads();  // every wave has read K_0 before step 0 refills its buffer with K_2
-
-  // Step j (K runs one tile ahead of V): prefetch K_{j+2} and V_{j+1}; then
-  //   [S_{j+1} = K_{j+1} Q^T on MFMA]  beside  [P_j = exp2(S_j - m) on the VALU]
-  //   [O += V_j^T P_j^T on MFMA]       beside  [max of S_{j+1}]
-  // The flags are compile-time so that the steady-state loop has no branch
-  // between the two regions: P = j % 2 (LDS buffers), NEXT = tile j+1 exists,
-  // TAIL = tile j+1 may be the ragged last tile, LOADK = tile j+2 exists.
-  auto step = [&](auto flags, int j, f32x16& c0, f32x16& c1, float& mt_c, f32x16& n0, f32x16& n1,
-                  float& mt_n) {
-    using Fl = decltype(flags);
-    constexpr int P = Fl::P;
-    // debug bit 2: the tiles this step copies exist
-    HA_CHECK((!Fl::LOADK || j + 2 < ntiles) && (!Fl::NEXT || j + 1 < ntiles), 2);
-    if constexpr (Fl::LOADK) issue_k(j + 2, P);
-    else if (j + 2 < ntiles) issue_k(j + 2, P);
-    if constexpr (Fl::NEXT) issue_v(j + 1, P ^ 1);
-    if (wave_active) {
-      rescale(mt_c);
-      uint32_t p0[8], p1[8];
-      if constexpr (Fl::NEXT) {
-        qk(kbuf + (P ^ 1) * C::TILE, n0, n1);
-        softmax_p(c0, c1, p0, p1);
-        interleave<2 * C::KSTEPS, PF, 1, 7>();
-        if constexpr (Fl::TAIL) {
-          if (j + 2 == ntiles && last_valid < KT) mask_tail(n0, n1);
+  // FUSED: the frame's counter, first read during the last key tile
+  unsigned fl_seen = 0;
+  if (tsplit) {
+    // ---- the short last query tile: waves 0 and 1 take key half `wave` of
+    // every tile (one tile of K and V in flight, all waves copying as in the
+    // main loop); their (max, sum, O) are merged into wave 0 at the end
+    auto qk1 = [&](const unsigned char* kb_, f32x16& s) {
+      s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
+        s = mfma32x32x16(*reinterpret_cast<const u32x4*>(kb_ + (kaddr ^ (ks << 5)) + wave * 32 * D * 2), qf[ks], s);
+    };
+    auto pv1 = [&](const unsigned char* vb_, const uint32_t* p) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int ra = 32 * wave + 16 * h2;
+          const u32x2 x0 = ds_read_tr16(vb_ + v_off(ra, db));
+          const u32x2 x1 = ds_read_tr16(vb_ + v_off(ra + 4, db));
+          o[db] = mfma32x32x16(u32x4{x0[0], x0[1], x1[0], x1[1]},
+                               u32x4{p[4 * h2], p[4 * h2 + 1], p[4 * h2 + 2], p[4 * h2 + 3]}, o[db]);
         }
-        pv(vbuf + P * C::TILE, p0, p1);
-        mt_n = tile_max(n0, n1);
-        interleave<4 * C::DB, PF, 2, 2>();
-      } else {
-        softmax_p(c0, c1, p0, p1);
-        pv(vbuf + P * C::TILE, p0, p1);
+    };
+    issue_k(0, 0);
+    issue_v(0, 0);
+    for (int t = 0; t < ntiles; ++t) {
+      const int pb = t & 1;
+      // tile t has landed and every wave is done with tile t-1's buffers
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 1 < ntiles) {
+        issue_k(t + 1, pb ^ 1);
+        issue_v(t + 1, pb ^ 1);
+      }
+      if constexpr (FUSED) {
+        if (t + 1 == ntiles && wave == 0 && lane == 0)
+          fl_seen = __hip_atomic_load(flags + ((size_t)(b * H + h) * F + n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const int valid = t + 1 == ntiles ? last_valid : KT;  // keys of this tile
+      if (wave_active && 32 * wave < valid) {  // this half holds at least one key
+        f32x16 s1;
+        qk1(kbuf + pb * C::TILE, s1);
+        if (valid < 32 * wave + 32) {
+          asm volatile("");
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * wave + 16 * (r >> 3) + 8 * hh + (r & 7) >= valid) s1[r] = -INFINITY;
+        }
+        float mt = s1[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s1[r]);
+        rescale(max_across_halves(mt) * c2);
+        uint32_t p1[8];
+        const float nm = -m_run;
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, nm));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(s1[r + 1], c2, nm));
+          a0 += x0;
+          a1 += x1;
+          p1[r >> 1] = pack_bf16x2(x0, x1);
+        }
+        l0 += a0 + a1;
+        pv1(vbuf + pb * C::TILE, p1);
       }
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_barrier();  // every wave is done with the last tile
     asm volatile("" ::: "memory");
-  };
-  // flags: <P, NEXT, TAIL, LOADK>
-  using Main0 = StepFlags<0, true, false, true>;
-  using Main1 = StepFlags<1, true, false, true>;
-
-  int j = 0;
-  for (; j + 3 < ntiles; j += 2) {
-    step(Main0{}, j, sa0, sa1, mt_a, sb0, sb1, mt_b);
-    step(Main1{}, j + 1, sb0, sb1, mt_b, sa0, sa1, mt_a);
-  }
-  // Remaining 1 to 3 tiles, without the software pipeline (one score tile
-  // live): S_t is in sa, V_t in buffer t % 2, K_{t+1} in buffer (t+1) % 2.
-  // FUSED: the frame's counter (below) is first read during the last tile,
-  // so that the device-scope load's latency hides behind the tile's work
-  unsigned fl_seen = 0;
-  for (int t = j; t < ntiles; ++t) {
-    const int pb = t & 1;
-    if constexpr (FUSED) {
-      if (t + 1 == ntiles && wave == 0 && lane == 0)
-        fl_seen = __hip_atomic_load(flags + ((size_t)(b * H + h) * F + n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // wave 1's (O, sum, max) through the V buffers, lane-major
+    float* mrg = reinterpret_cast<float*>(vbuf);
+    static_assert((C::DB * 16 + 2) * 64 * 4 <= 2 * C::TILE, "the merge must fit in the V buffers");
+    if (wave == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mrg[(db * 16 + r) * 64 + lane] = o[db][r];
+      mrg[C::DB * 16 * 64 + lane] = l0;
+      mrg[(C::DB * 16 + 1) * 64 + lane] = m_run;
     }
-    if (t + 1 < ntiles) issue_v(t + 1, pb ^ 1);
-    if (t + 2 < ntiles) issue_k(t + 2, pb);
+    __syncthreads();
+    if (wave == 0) {
+      const float l_1 = mrg[C::DB * 16 * 64 + lane], m_1 = mrg[(C::DB * 16 + 1) * 64 + lane];
+      const float mn = fmaxf(m_run, m_1);  // wave 0's half always holds a key: finite
+      const float f0 = __builtin_amdgcn_exp2f(m_run - mn), f1 = __builtin_amdgcn_exp2f(m_1 - mn);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = fmaf(o[db][r], f0, mrg[(db * 16 + r) * 64 + lane] * f1);
+      l0 = fmaf(l0, f0, l_1 * f1);
+      m_run = mn;
+    }
+    wave_active = wave_active && wave == 0;
+  } else {
+    // ---- prologue: K_0, V_0, K_1 in flight, then S_0
+    issue_k(0, 0);
+    issue_v(0, 0);
+    if (ntiles > 1) issue_k(1, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 sa0, sa1, sb0, sb1;
+    float mt_a = 0.f, mt_b = 0.f;
     if (wave_active) {
-      rescale(mt_a);
-      uint32_t p0[8], p1[8];
-      softmax_p(sa0, sa1, p0, p1);
-      pv(vbuf + pb * C::TILE, p0, p1);
-      if (t + 1 < ntiles) {
-        qk(kbuf + (pb ^ 1) * C::TILE, sa0, sa1);
-        if (t + 2 == ntiles && last_valid < KT) mask_tail(sa0, sa1);
-        mt_a = tile_max(sa0, sa1);
+      qk(kbuf, sa0, sa1);
+      if (ntiles == 1 && last_valid < KT) mask_tail(sa0, sa1);
+      mt_a = tile_max(sa0, sa1);
+    }
+    __syncthreads();  // every wave has read K_0 before step 0 refills its buffer with K_2
+
+    // Step j (K runs one tile ahead of V): prefetch K_{j+2} and V_{j+1}; then
+    //   [S_{j+1} = K_{j+1} Q^T on MFMA]  beside  [P_j = exp2(S_j - m) on the VALU]
+    //   [O += V_j^T P_j^T on MFMA]       beside  [max of S_{j+1}]
+    // The flags are compile-time so that the steady-state loop has no branch
+    // between the two regions: P = j % 2 (LDS buffers), NEXT = tile j+1 exists,
+    // TAIL = tile j+1 may be the ragged last tile, LOADK = tile j+2 exists.
+    auto step = [&](auto flags, int j, f32x16& c0, f32x16& c1, float& mt_c, f32x16& n0, f32x16& n1,
+                    float& mt_n) {
+      using Fl = decltype(flags);
+      constexpr int P = Fl::P;
+      // debug bit 2: the tiles this step copies exist
+      HA_CHECK((!Fl::LOADK || j + 2 < ntiles) && (!Fl::NEXT || j + 1 < ntiles), 2);
+      if constexpr (Fl::LOADK) issue_k(j + 2, P);
+      else if (j + 2 < ntiles) issue_k(j + 2, P);
+      if constexpr (Fl::NEXT) issue_v(j + 1, P ^ 1);
+      if (wave_active) {
+        rescale(mt_c);
+        uint32_t p0[8], p1[8];
+        if constexpr (Fl::NEXT) {
+          qk(kbuf + (P ^ 1) * C::TILE, n0, n1);
+          softmax_p(c0, c1, p0, p1);
+          interleave<2 * C::KSTEPS, PF, 1, 7>();
+          if constexpr (Fl::TAIL) {
+            if (j + 2 == ntiles && last_valid < KT) mask_tail(n0, n1);
+          }
+          pv(vbuf + P * C::TILE, p0, p1);
+          mt_n = tile_max(n0, n1);
+          interleave<4 * C::DB, PF, 2, 2>();
+        } else {
+          softmax_p(c0, c1, p0, p1);
+          pv(vbuf + P * C::TILE, p0, p1);
+        }
       }
-    }
-    asm volatile("" ::: "memory");
-    if constexpr (FUSED) {
-      // the last tile copies nothing: wait for LDS only, the counter load may stay in flight
-      if (t + 1 == ntiles) __builtin_amdgcn_s_waitcnt(0xC07F);
-      else __builtin_amdgcn_s_waitcnt(0);
-    } else {
+      asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // flags: <P, NEXT, TAIL, LOADK>
+    using Main0 = StepFlags<0, true, false, true>;
+    using Main1 = StepFlags<1, true, false, true>;
+
+    int j = 0;
+    for (; j + 3 < ntiles; j += 2) {
+      step(Main0{}, j, sa0, sa1, mt_a, sb0, sb1, mt_b);
+      step(Main1{}, j + 1, sb0, sb1, mt_b, sa0, sa1, mt_a);
     }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    // Remaining 1 to 3 tiles, without the software pipeline (one score tile
+    // live): S_t is in sa, V_t in buffer t % 2, K_{t+1} in buffer (t+1) % 2.
+    // FUSED: the frame's counter (below) is first read during the last tile,
+    // so that the device-scope load's latency hides behind the tile's work
+    for (int t = j; t < ntiles; ++t) {
+      const int pb = t & 1;
+      if constexpr (FUSED) {
+        if (t + 1 == ntiles && wave == 0 && lane == 0)
+          fl_seen = __hip_atomic_load(flags + ((size_t)(b * H + h) * F + n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (t + 1 < ntiles) issue_v(t + 1, pb ^ 1);
+      if (t + 2 < ntiles) issue_k(t + 2, pb);
+      if (wave_active) {
+        rescale(mt_a);
+        uint32_t p0[8], p1[8];
+        softmax_p(sa0, sa1, p0, p1);
+        pv(vbuf + pb * C::TILE, p0, p1);
+        if (t + 1 < ntiles) {
+          qk(kbuf + (pb ^ 1) * C::TILE, sa0, sa1);
+          if (t + 2 == ntiles && last_valid < KT) mask_tail(sa0, sa1);
+          mt_a = tile_max(sa0, sa1);
+        }
+      }
+      asm volatile("" ::: "memory");
+      if constexpr (FUSED) {
+        // the last tile copies nothing: wait for LDS only, the counter load may stay in flight
+        if (t + 1 == ntiles) __builtin_amdgcn_s_waitcnt(0xC07F);
+        else __builtin_amdgcn_s_waitcnt(0);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+
   }
 
   if constexpr (KV) {  // ---- epilogue without readout

@@ -160,70 +160,97 @@ __global__ __launch_bounds__(NT) void gram_bf16_kernel(const uint16_t* __restric
            1);
   HA_CHECK(tr_off(16 * (KSC - 1) + 4, NRB - 1) + 8 <= TILE, 2);
   for (int c = 0; c < NBUF - 1 && c < nch; ++c) issue(c0 + c, c);
-  // TB < 0: every G block; TB >= 0: this wave's band is TB, G blocks cb >= TB
+  // this wave's copies per chunk (K' and V' segments, and beta)
+  constexpr int PER = 2 * MY_SEGS;
+  static_assert(2 * (PER + 1) <= 15, "vmcnt field");
+  // wait until at most `later` chunks after the awaited one are in flight
+  auto wait_chunks = [&](int later) {
+    if (has_beta) {
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (PER + 1)));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (PER + 1));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | PER);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+  };
+  constexpr int KPW = KSC / KH;  // k-steps of a chunk per wave
+  // TB < 0: every G block; TB >= 0: this wave's band is TB, G blocks cb >= TB.
+  // The A operands of a chunk, (beta K')^T rows 32*band.., tokens 16*ks +
+  // 8*hh + e split into bf16 hi + lo, are formed while the MFMAs of the chunk
+  // before it run: the barrier at the top of step c makes chunk c + 1
+  // visible, so no wave starts a chunk with its operand arithmetic.
   auto chunks = [&](auto tb_c) {
     constexpr int TB = decltype(tb_c)::value;
     const int band = TB >= 0 ? TB : rb;
+    // A operands of k-step kk of the chunk in buffer buf (shared by the G
+    // blocks, B operand K', and the B blocks, B operand V'; with two step-size
+    // vectors the B blocks take their own (beta2 K')^T)
+    auto prep = [&](int buf, int kk, u32x4& ahi, u32x4& alo, u32x4& bhi, u32x4& blo) {
+      const unsigned char* kt = smem + buf * BUF;
+      const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
+      const int ks = kh * KPW + kk;
+      const u32x4 kraw = tr8(kt, ks, band);
+      auto scaled_split = [&](const float* bp, u32x4& hi4, u32x4& lo4) {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh + 4);
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const float bl = w2 < 2 ? b0[2 * w2] : b1[2 * w2 - 4];
+          const float bu = w2 < 2 ? b0[2 * w2 + 1] : b1[2 * w2 - 3];
+          const float x0 = bl * bf16_lo_to_f32(kraw[w2]);
+          const float x1 = bu * bf16_hi_to_f32(kraw[w2]);
+          const uint32_t hi = pack_bf16x2(x0, x1);
+          hi4[w2] = hi;
+          lo4[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
+        }
+      };
+      scaled_split(be, ahi, alo);
+      if constexpr (TWO) scaled_split(be + TC, bhi, blo);
+      else { bhi = ahi; blo = alo; }
+    };
+    u32x4 ahi[KPW], alo[KPW], bhi[KPW], blo[KPW];
+    if (nch > 0) {
+      // chunk 0 landed (chunks 1 and 2 may be in flight) and is visible
+      wait_chunks(nch - 1 < NBUF - 2 ? nch - 1 : NBUF - 2);
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < KPW; ++kk) prep(0, kk, ahi[kk], alo[kk], bhi[kk], blo[kk]);
+    }
     for (int c = 0; c < nch; ++c) {
       const int buf = c % NBUF;
-      // chunk c landed: at most the loads of the chunks after it are outstanding
-      const int later = (nch - 1 - c) < (NBUF - 2) ? (nch - 1 - c) : (NBUF - 2);
-      if (has_beta) {
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (2 * MY_SEGS + 1)));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS + 1));
-        else __builtin_amdgcn_s_waitcnt(0x0F70);
-      } else {
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * 2 * MY_SEGS));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * MY_SEGS));
-        else __builtin_amdgcn_s_waitcnt(0x0F70);
+      const bool more = c + 1 < nch;
+      if (more) {
+        // chunk c+1 landed (chunk c+2 may be in flight), and every wave is
+        // done with chunk c-1, whose buffer takes chunk c+NBUF-1
+        wait_chunks(nch - 2 - c < 1 ? nch - 2 - c : 1);
+        __syncthreads();
+        if (c + NBUF - 1 < nch) issue(c0 + c + NBUF - 1, (c + NBUF - 1) % NBUF);
       }
-      __syncthreads();
-      // the buffer of chunk c-1 is free (every wave passed the barrier above
-      // after consuming it): refill it with chunk c+NBUF-1
-      if (c + NBUF - 1 < nch) issue(c0 + c + NBUF - 1, (c + NBUF - 1) % NBUF);
       const unsigned char* kt = smem + buf * BUF;
       const unsigned char* vt = kt + TILE;
-      const float* be = reinterpret_cast<const float*>(kt + 2 * TILE);
-      const float* be2 = be + (TWO ? TC : 0);
 #pragma unroll
-      for (int kk = 0; kk < KSC / KH; ++kk) {
-        const int ks = kh * (KSC / KH) + kk;
-        // A = (beta K')^T rows 32*rb.., tokens 16*ks + 8*hh + e: split hi + lo,
-        // shared by the G blocks (B operand K') and the B blocks (B operand V');
-        // with two step-size vectors the B blocks take their own (beta2 K')^T
-        const u32x4 kraw = tr8(kt, ks, band);
-        auto scaled_split = [&](const float* bp, u32x4& hi4, u32x4& lo4) {
-          const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh);
-          const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 16 * ks + 8 * hh + 4);
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) {
-            const float bl = w2 < 2 ? b0[2 * w2] : b1[2 * w2 - 4];
-            const float bu = w2 < 2 ? b0[2 * w2 + 1] : b1[2 * w2 - 3];
-            const float x0 = bl * bf16_lo_to_f32(kraw[w2]);
-            const float x1 = bu * bf16_hi_to_f32(kraw[w2]);
-            const uint32_t hi = pack_bf16x2(x0, x1);
-            hi4[w2] = hi;
-            lo4[w2] = pack_bf16x2(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
-          }
-        };
-        u32x4 ahi, alo, bhi, blo;
-        scaled_split(be, ahi, alo);
-        if constexpr (TWO) scaled_split(be2, bhi, blo);
-        else { bhi = ahi; blo = alo; }
+      for (int kk = 0; kk < KPW; ++kk) {
+        const int ks = kh * KPW + kk;
 #pragma unroll
         for (int cb = 0; cb < NRB; ++cb) {
           const u32x4 bv = tr8(vt, ks, cb);
           if (TB < 0 || cb >= TB) {
             const u32x4 bk = tr8(kt, ks, cb);
-            ag[cb] = mfma32x32x16(ahi, bk, ag[cb]);
-            ab[cb] = mfma32x32x16(bhi, bv, ab[cb]);
-            ag[cb] = mfma32x32x16(alo, bk, ag[cb]);
-            ab[cb] = mfma32x32x16(blo, bv, ab[cb]);
+            ag[cb] = mfma32x32x16(ahi[kk], bk, ag[cb]);
+            ab[cb] = mfma32x32x16(bhi[kk], bv, ab[cb]);
+            ag[cb] = mfma32x32x16(alo[kk], bk, ag[cb]);
+            ab[cb] = mfma32x32x16(blo[kk], bv, ab[cb]);
           } else {
-            ab[cb] = mfma32x32x16(bhi, bv, ab[cb]);
-            ab[cb] = mfma32x32x16(blo, bv, ab[cb]);
+            ab[cb] = mfma32x32x16(bhi[kk], bv, ab[cb]);
+            ab[cb] = mfma32x32x16(blo[kk], bv, ab[cb]);
           }
         }
+        // this k-step's operands are consumed: form chunk c+1's (after the
+        // last chunk from a stale buffer, unused; no branch keeps the
+        // arithmetic free to interleave with the MFMAs above)
+        prep((c + 1) % NBUF, kk, ahi[kk], alo[kk], bhi[kk], blo[kk]);
       }
     }
   };
