@@ -245,9 +245,10 @@ __global__ __launch_bounds__(256) void tl_prep_kernel(const uint16_t* __restrict
 // Per chunk: S to LDS as split B fragments; waves 0, 1 form X = U - W S for
 // token block w, waves 2, 3 Q S for token block w - 2; X to LDS as split B
 // fragments; waves 2, 3 write the inter-frame output c (Q S) + P X (fp32);
-// every wave advances its rows S = a S + K^T X. The next chunk's operands are
-// loaded into registers while the current one computes (the barriers order
-// LDS only, so those loads stay in flight).
+// every wave advances its rows S = a S + K^T X. Two register sets of operands
+// alternate between the chunks: each part of a set is reloaded with the
+// operands of the chunk two ahead as soon as its chunk has used it (the
+// barriers order LDS only, so those loads stay in flight).
 struct TlOps {
   u32x4 big[16];  // waves 0, 1: -W fragments [ks][hi/lo]; waves 2, 3: Q [ks] then P [ks][hi/lo]
   f32x16 u;       // waves 0, 1: U block
@@ -272,7 +273,11 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
   const int nc = F * nchf;
   const int tb = w & 1;
 
-  auto load = [&](int c, TlOps& o) {
+  // the operands of chunk c, in three parts, each loaded into a register set
+  // as soon as the chunk that set serves no longer reads that part:
+  // part 0, the X or Q S phase (waves 0, 1: -W and U; waves 2, 3: Q rows);
+  // part 1, the output phase (waves 2, 3: P); part 2, the state advance (K^T)
+  auto load = [&](int c, TlOps& o, int part) {
     const int n = c / nchf, ci = c % nchf;
     const int t0 = n * L + ci * TLC;
     const int m = L - ci * TLC < TLC ? L - ci * TLC : TLC;
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
     const f32x4* uc = reinterpret_cast<const f32x4*>(fr + WF_B);
     const u32x4* pf = reinterpret_cast<const u32x4*>(fr + WF_B + UC_B);
     const u32x4* kf = reinterpret_cast<const u32x4*>(fr + WF_B + UC_B + PF_B);
-    if (w < 2) {
+    if (part == 0 && w < 2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) o.big[i] = wf[((tb * 8 + (i >> 1)) * 2 + (i & 1)) * 64 + lane];
 #pragma unroll
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
         const f32x4 x = uc[((tb * 4 + cb) * 64 + lane) * 4 + v4];
         o.u[4 * v4] = x[0]; o.u[4 * v4 + 1] = x[1]; o.u[4 * v4 + 2] = x[2]; o.u[4 * v4 + 3] = x[3];
       }
-    } else {
+    } else if (part == 0) {
       const int i = 32 * tb + lr;
       const uint16_t* qrow = qp + ((size_t)b * T + t0 + (i < m ? i : m - 1)) * rs + (size_t)h * TLD;
 #pragma unroll
@@ -299,21 +304,21 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
         const u32x2 q1 = *reinterpret_cast<const u32x2*>(qrow + c0 + 8);
         o.big[ks] = u32x4{q0[0], q0[1], q1[0], q1[1]};
       }
+    } else if (part == 1 && w >= 2) {
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) o.big[8 + i2] = pf[((tb * 4 + (i2 >> 1)) * 2 + (i2 & 1)) * 64 + lane];
-    }
+    } else if (part == 2) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.kk[ks] = kf[(w * 4 + ks) * 64 + lane];
+      for (int ks = 0; ks < 4; ++ks) o.kk[ks] = kf[(w * 4 + ks) * 64 + lane];
+    }
   };
 
-  TlOps cur, nxt;
-  load(0, cur);
-  for (int c = 0; c < nc; ++c) {
+  // chunk c on register set cur, which then takes chunk pf (pf < nc)
+  auto chunk = [&](int c, TlOps& cur, int pf) {
     const int n = c / nchf, ci = c % nchf;
     const int t0 = n * L + ci * TLC;
     const int m = L - ci * TLC < TLC ? L - ci * TLC : TLC;
     const float dec = ci == 0 ? alpha[((size_t)b * F + n) * H + h] : 1.0f;
-    if (c + 1 < nc) load(c + 1, nxt);
 
     // S -> LDS: registers [8s, 8s + 8) are the B operand of k-step 2w + s
 #pragma unroll
@@ -355,6 +360,7 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
         acc = mfma32x32x16(cur.big[ks], sfr[ks][1][lane], acc);
       }
     }
+    if (pf < nc) load(pf, cur, 0);
     lds_barrier();
     if (w >= 2) {  // out_i = c_i (Q S)_i + sum_{j<i} P_ij X_j
 #pragma unroll
@@ -375,6 +381,7 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
         if (i < m) o_inter[((size_t)b * T + t0 + i) * rs + (size_t)h * TLD + 32 * cb + lr] = acc[r];
       }
     }
+    if (pf < nc) load(pf, cur, 1);
     // S rows of wave w: a S + K^T X
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] *= dec;
@@ -383,8 +390,18 @@ __global__ __launch_bounds__(256) void tl_scan_kernel(const unsigned char* __res
       S = mfma32x32x16(cur.kk[ks], xfr[ks][0][lane], S);
       S = mfma32x32x16(cur.kk[ks], xfr[ks][1][lane], S);
     }
+    if (pf < nc) load(pf, cur, 2);
     lds_barrier();
-    cur = nxt;
+  };
+  TlOps o0, o1;
+#pragma unroll
+  for (int part = 0; part < 3; ++part) {
+    load(0, o0, part);
+    if (nc > 1) load(1, o1, part);
+  }
+  for (int c = 0; c < nc; c += 2) {
+    chunk(c, o0, c + 2);
+    if (c + 1 < nc) chunk(c + 1, o1, c + 3);
   }
   if (update_state) {
 #pragma unroll
