@@ -46,6 +46,11 @@
 // takes 64 bytes per clock). A fifth wave then issues every copy and the four
 // compute waves only compute; the step barrier still orders the buffers.
 //
+// Short last query tile: when a work-group's query tile holds at most 32
+// queries (1560 = 12 x 128 + 24), waves 0 and 1 both take them, each with one
+// 32-key half of every key tile, and merge their (max, sum, O) through LDS
+// before the readout, instead of one wave walking all keys while three idle.
+//
 // Fused scan (FUSED, forward calls over several frames): the first
 // work-groups of the launch run the clean pass's state scan (scan_role below)
 // and publish S_{n-1} of every frame as readout fragments; an attention
@@ -529,8 +534,8 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
   unsigned fl_seen = 0;
   if (tsplit) {
     // ---- the short last query tile: waves 0 and 1 take key half `wave` of
-    // every tile (one tile of K and V in flight, all waves copying as in the
-    // main loop); their (max, sum, O) are merged into wave 0 at the end
+    // every tile (one tile of K and V in flight, copied by the same waves as
+    // in the main loop); their (max, sum, O) are merged into wave 0 at the end
     auto qk1 = [&](const unsigned char* kb_, f32x16& s) {
       s = f32x16{};
 #pragma unroll
