@@ -105,6 +105,24 @@ def test_edge_lengths_without_loader_wave(d, L, F, H):
     assert eo < TOL_OUT and es < TOL_STATE
 
 
+# --- the short last query tile: two waves, one 32-key half each ------------
+# A query tile of at most 32 queries (L - 128 qt <= 32) splits its keys over
+# waves 0 and 1 and merges their (max, sum, O); 33 queries or more take the
+# usual loop. Both sides of the boundary, with and without the loader wave
+# (up to 256 work-groups), ragged and full last key tiles.
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,F,H", [(32, 2, 2), (33, 2, 2), (160, 2, 2), (161, 2, 2), (192, 3, 2),
+                                   (160, 17, 8), (161, 17, 8), (1560, 2, 2)])
+def test_short_last_query_tile(d, L, F, H):
+    w = small("480p", B=1, H=H, d=d, L=L, frames=F, state0_sigma=0.05)
+    tail = L - (L - 1) // 128 * 128
+    say(f"case short last query tile d={d} L={L} (tail {tail} queries) F={F} H={H}")
+    eo, es, *_ = full_compare(w)
+    say(f"  rel_err out {eo:.3e} state {es:.3e}")
+    assert eo < TOL_OUT and es < TOL_STATE
+
+
 # --- many frames: one gram work-group per (stream, head, frame) ----------------
 
 @pytest.mark.parametrize("d", [64, 128])
