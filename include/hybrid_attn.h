@@ -225,9 +225,9 @@ ha_status hybrid_attn_state_update(const void* kp, const void* vp,
  * readout fragments): with update_state = 0, d x d bf16 per (stream, head);
  * otherwise per (stream, head, frame) the state increments (d x 2d fp32), the
  * fp32 partial sums of n token splits (n as for hybrid_attn_workspace_bytes,
- * at least 1; d x 2d fp32 each), the pre-update state S_{N-1} (d x d fp32) and
- * its readout fragments (d x d bf16), each region 256-byte aligned. Returns 0
- * for invalid sizes.
+ * at least 1; d x 2d fp32 each), the pre-update state S_{N-1} (d x d fp32),
+ * its readout fragments (d x d bf16) and a 4-byte frame counter, each region
+ * 256-byte aligned. Returns 0 for invalid sizes.
  */
 size_t hybrid_attn_fmap_workspace_bytes(int B, int H, int T, int frame_len, int d,
                                         int update_state);

@@ -132,7 +132,8 @@ def test_feature_map_and_gated_workspace_sizes():
     T = F * L
     up = lambda x: (x + 255) // 256 * 256
     gf = H * F * d * 2 * d * 4
-    fmap1 = up(gf) + up(gf) + up(H * F * d * d * 4) + up(H * F * d * d * 2)
+    # increments, partial sums, fp32 snapshots, readout fragments, frame counters
+    fmap1 = up(gf) + up(gf) + up(H * F * d * d * 4) + up(H * F * d * d * 2) + up(H * F * 4)
     assert api.fmap_workspace_bytes(1, H, T, L, d, 0) == up(H * d * d * 2)
     assert api.fmap_workspace_bytes(1, H, T, L, d, 1) == fmap1
     # gated: beta, beta / n^2, beta / n, per-64-token-chunk alpha sums (25 chunks

@@ -139,11 +139,18 @@ constexpr int kSpinLimit = 1 << 22;      // polls of a frame counter (a guard: i
 // readout fragments of frame n with device-scope stores; after the next
 // barrier (each wave's stores acknowledged before it) one lane adds one to
 // flags[bh*F + n]. The last state goes to state (fp32).
-template <int D>
+// FM (the layer with per-head feature maps, Q' = Q W_q): the readout
+// fragments of frame n are those of M_n = W_q S_{n-1} instead (the readout
+// then contracts Q with M_n): wave w computes row band w of M_n[:, cb] from
+// the S exchange in LDS and its band of W_q (bf16 A fragments held in
+// registers, in the exchange's contraction order), and the counter of frame
+// n is raised at the step after, once those fragments are stored.
+template <int D, bool FM = false>
 __device__ __forceinline__ void scan_role(const unsigned char* __restrict__ ws, const float* __restrict__ alpha,
                                           float* __restrict__ state, unsigned char* __restrict__ sfrag,
                                           unsigned* __restrict__ flags, int bh, int cb, int H, int F,
-                                          unsigned char* smem, int wave, int lane) {
+                                          unsigned char* smem, int wave, int lane,
+                                          const uint16_t* __restrict__ wq = nullptr) {
   constexpr int NRB = D / 32, NCB = D / 32, KS = D / 16;
   constexpr size_t PER = (size_t)D * D * 8;  // increment bytes per (b, h, frame)
   u32x4(*lds)[2][KS][64] = reinterpret_cast<u32x4(*)[2][KS][64]>(smem);  // [slot][hi, lo][k-step][lane]
@@ -158,6 +165,18 @@ __device__ __forceinline__ void scan_role(const unsigned char* __restrict__ ws, 
   if (comp) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col];
+  }
+  // FM: row band w of W_q (head h) as A fragments: k-slot 8*hh + e of k-step
+  // ks holds column 16*ks + 8*(e/4) + 4*hh + e%4
+  u32x4 wqa[FM ? KS : 1];
+  if constexpr (FM) {
+    const uint16_t* W = wq + (size_t)h * D * D + (size_t)(row0 + lr) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(W + 16 * ks + 4 * hh);
+      const u32x2 a1 = *reinterpret_cast<const u32x2*>(W + 16 * ks + 8 + 4 * hh);
+      wqa[ks] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    }
   }
   u32x4 gh[KS], gl[KS];
   f32x4 bv[2][4];
@@ -194,8 +213,9 @@ __device__ __forceinline__ void scan_role(const unsigned char* __restrict__ ws, 
       }
       lds[SL][0][2 * w + sh][lane] = hi;
       lds[SL][1][2 * w + sh][lane] = lo;
-      __builtin_amdgcn_raw_buffer_store_b128(hi, rsf, (uint32_t)((((n * NCB + cb) * KS) + 2 * w + sh) * 64 + lane) * 16, 0,
-                                             kDevice);
+      if constexpr (!FM)
+        __builtin_amdgcn_raw_buffer_store_b128(hi, rsf, (uint32_t)((((n * NCB + cb) * KS) + 2 * w + sh) * 64 + lane) * 16,
+                                               0, kDevice);
     }
   };
   if (comp) {
@@ -212,8 +232,29 @@ __device__ __forceinline__ void scan_role(const unsigned char* __restrict__ ws, 
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (wave == 0 && lane == 0) __hip_atomic_fetch_add(flags + (size_t)bh * F + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (FM) {  // M_{n-1}'s fragments, computed in the step before, are stored
+      if (n > 0 && wave == 0 && lane == 0)
+        __hip_atomic_fetch_add(flags + (size_t)bh * F + n - 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (wave == 0 && lane == 0) __hip_atomic_fetch_add(flags + (size_t)bh * F + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (comp) {
+      if constexpr (FM) {  // M_n = W_q S_{n-1}, row band w, from the exchange
+        f32x16 m = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          m = mfma32x32x16(wqa[ks], lds[SL][0][ks][lane], m);
+          m = mfma32x32x16(wqa[ks], lds[SL][1][ks][lane], m);
+        }
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          u32x4 hi;
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) hi[w2] = pack_bf16x2(m[8 * sh + 2 * w2], m[8 * sh + 2 * w2 + 1]);
+          __builtin_amdgcn_raw_buffer_store_b128(hi, rsf, (uint32_t)((((n * NCB + cb) * KS) + 2 * w + sh) * 64 + lane) * 16,
+                                                 0, kDevice);
+        }
+      }
       f32x16 nacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) nacc[r] = fmaf(al[SL], acc[r], bv[SL][r >> 2][r & 3]);
@@ -239,6 +280,14 @@ __device__ __forceinline__ void scan_role(const unsigned char* __restrict__ ws, 
     step(S1{}, n + 1);
   }
   if (n < F) step(S0{}, n);
+  if constexpr (FM) {  // the last frame's M fragments are stored
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (wave == 0 && lane == 0)
+      __hip_atomic_fetch_add(flags + (size_t)bh * F + F - 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (comp) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sbase[(size_t)(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + col] = acc[r];
@@ -260,7 +309,8 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
     int qtiles, int n_items, float c2 /* softmax scale * log2(e) */,
     int Tk, int kv_off, int nsplit, float* __restrict__ part_o, float2* __restrict__ part_ml,
     const float* __restrict__ add_o, const float* __restrict__ mix, const unsigned char* __restrict__ gws,
-    const float* __restrict__ alpha, float* __restrict__ state, unsigned* __restrict__ flags, int n_scan) {
+    const float* __restrict__ alpha, float* __restrict__ state, unsigned* __restrict__ flags, int n_scan,
+    const uint16_t* __restrict__ wq) {
   using C = Cfg<D>;
   constexpr int NCH = C::NCH;
   __shared__ __align__(16) unsigned char smem[C::SMEM];
@@ -292,8 +342,13 @@ __global__ __launch_bounds__(LOADER ? NT + kWave : NT, LOADER ? 1 : 2) void attn
         constexpr int NCB = D / 32;
         const int si = (g & 7) * (n_scan >> 3) + (g >> 3);
         if (si >= n_items / (F * qtiles) * NCB) return;
-        scan_role<D>(gws, alpha, state, const_cast<unsigned char*>(sfrag), flags, si / NCB, si % NCB, H, F, smem,
-                     __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), (int)threadIdx.x & 63);
+        // with per-head feature maps (wq) the readout fragments are those of W_q S
+        const int sw = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), sl = (int)threadIdx.x & 63;
+        if (wq)
+          scan_role<D, true>(gws, alpha, state, const_cast<unsigned char*>(sfrag), flags, si / NCB, si % NCB, H, F, smem,
+                             sw, sl, wq);
+        else
+          scan_role<D>(gws, alpha, state, const_cast<unsigned char*>(sfrag), flags, si / NCB, si % NCB, H, F, smem, sw, sl);
         return;
       }
       const int ga = g - n_scan;
@@ -958,7 +1013,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
                               (const uint16_t*)qp, states, stride_bh, stride_frame,
                               (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
                               qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr, mix, nullptr, nullptr,
-                              nullptr, nullptr, 0);
+                              nullptr, nullptr, 0, nullptr);
   };
   if (mix) {
     if (s.d == 128) loader ? args(attn_bf16_kernel<128, false, true, true>) : args(attn_bf16_kernel<128, false, true>);
@@ -972,7 +1027,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
 
 hipError_t launch_attn_scan_bf16(const void* q, const void* k, const void* v, const void* qp, const void* ws,
                                  const float* alpha, float* state, void* sfrag, unsigned* flags, void* out,
-                                 const Shape& s, float scale, hipStream_t st) {
+                                 const Shape& s, float scale, hipStream_t st, const void* wq) {
   const int qtiles = (s.L + QPB - 1) / QPB;
   const long long items = (long long)s.B * s.H * s.F * qtiles;
   const int ncb = s.d / 32;
@@ -983,13 +1038,14 @@ hipError_t launch_attn_scan_bf16(const void* q, const void* k, const void* v, co
   const long long fb = (long long)s.d * s.d * 2;  // fragment bytes per frame
   HA_LOG("launch attn_bf16_kernel<%d> with the state scan: grid %d x %d threads (%d scan work-groups for %d (b, h, "
          "column block) units walking %d frames, then %lld attention items = %d streams x %d heads x %d frames x %d "
-         "query tiles; each waits for its frame's state)",
-         s.d, grid, NT, n_scan, units, s.F, items, s.B, s.H, s.F, qtiles);
+         "query tiles; each waits for its frame's state%s)",
+         s.d, grid, NT, n_scan, units, s.F, items, s.B, s.H, s.F, qtiles,
+         wq ? "; readout fragments of W_q S, contracted with Q" : "");
   auto args = [&](auto kern) {
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)qp,
                               nullptr, s.F * fb, fb, (const unsigned char*)sfrag, (uint16_t*)out, s.H, s.T, s.L, s.F,
                               qtiles, (int)items, c2, s.T, 0, 1, nullptr, nullptr, nullptr, nullptr,
-                              (const unsigned char*)ws, alpha, state, flags, n_scan);
+                              (const unsigned char*)ws, alpha, state, flags, n_scan, (const uint16_t*)wq);
   };
   if (s.d == 128) args(attn_bf16_kernel<128, false, false, false, true>);
   else args(attn_bf16_kernel<64, false, false, false, true>);
@@ -1021,7 +1077,7 @@ hipError_t launch_attn_kv_bf16(const void* q, const void* k_cache, const void* v
     kern<<<grid, NT, 0, st>>>((const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
                               nullptr, 0, 0, nullptr, (uint16_t*)out, s.H, s.T, s.L, s.F, qtiles, units, c2, Tk,
                               kv_off, nsplit, part_o, (float2*)part_ml, add_o, nullptr, nullptr, nullptr, nullptr, nullptr,
-                              0);
+                              0, nullptr);
   };
   if (s.d == 128) args(attn_bf16_kernel<128, true>);
   else args(attn_bf16_kernel<64, true>);

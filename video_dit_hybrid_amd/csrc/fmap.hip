@@ -81,7 +81,8 @@ __global__ __launch_bounds__(D / 32 * 64) void gram_fmap_kernel(const float* __r
                                                                 int nsplit,
                                                                 const uint16_t* __restrict__ wk,
                                                                 const uint16_t* __restrict__ wv,
-                                                                float* __restrict__ gram, int H, int F) {
+                                                                float* __restrict__ gram, int H, int F,
+                                                                unsigned* __restrict__ flags) {
   constexpr int NRB = D / 32, KS = D / 16, NTH = NRB * 64;
   __shared__ __align__(16) unsigned char smem[2 * D * D * 2 + D * D * 4];
   unsigned char* const wkl = smem;
@@ -93,6 +94,8 @@ __global__ __launch_bounds__(D / 32 * 64) void gram_fmap_kernel(const float* __r
   const int h = hf % H, n = (hf / H) % F, b = hf / (H * F);
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the frame's counter of a scan fused into the attention launch starts at zero
+  if (flags && tid == 0) flags[((size_t)b * H + h) * F + n] = 0u;
 
   stage_w<D>(wkl, wk + (size_t)h * D * D, tid, NTH);
   stage_w<D>(wvl, wv + (size_t)h * D * D, tid, NTH);
@@ -404,15 +407,15 @@ __global__ __launch_bounds__(256) void keyscale_kernel(const uint16_t* __restric
 }  // namespace
 
 hipError_t launch_gram_fmap(const float* partial, int nsplit, const void* wk, const void* wv, float* gram,
-                            const Shape& s, hipStream_t st) {
+                            const Shape& s, hipStream_t st, unsigned* flags) {
   const int groups = s.B * s.H * s.F;
   HA_LOG("launch gram_fmap_kernel<%d>: grid %d (sums of %d token splits, then the maps)", s.d, groups, nsplit);
   if (s.d == 128)
     gram_fmap_kernel<128><<<groups, 256, 0, st>>>(partial, nsplit, (const uint16_t*)wk, (const uint16_t*)wv,
-                                                  gram, s.H, s.F);
+                                                  gram, s.H, s.F, flags);
   else
     gram_fmap_kernel<64><<<groups, 128, 0, st>>>(partial, nsplit, (const uint16_t*)wk, (const uint16_t*)wv,
-                                                 gram, s.H, s.F);
+                                                 gram, s.H, s.F, flags);
   return hipGetLastError();
 }
 

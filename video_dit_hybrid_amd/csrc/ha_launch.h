@@ -33,11 +33,13 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const v
 // the increments ws written by launch_gram_bf16, advancing state to S_F),
 // publishing each S_{n-1} as readout fragments to sfrag (strides F*d*d*2 and
 // d*d*2 bytes) and counting each frame's published column blocks in
-// flags[(b*H + h)*F + n], which launch_gram_bf16 zeroed; the attention
-// work-groups of frame n wait for that count before their readout.
+// flags[(b*H + h)*F + n], which launch_gram_bf16 (or launch_gram_fmap)
+// zeroed; the attention work-groups of frame n wait for that count before
+// their readout. With wq (per-head maps [H][d][d] bf16) the fragments are
+// those of W_q S_{n-1}, and qp is the unmapped Q.
 hipError_t launch_attn_scan_bf16(const void* q, const void* k, const void* v, const void* qp, const void* ws,
                                  const float* alpha, float* state, void* sfrag, unsigned* flags, void* out,
-                                 const Shape& s, float scale, hipStream_t st);
+                                 const Shape& s, float scale, hipStream_t st, const void* wq = nullptr);
 
 // KV mode of the same kernel (the softmax teacher with a full KV cache): the
 // queries of call frame n (q, out [B, T, H, d], T = F * L) attend to the keys
@@ -87,7 +89,7 @@ hipError_t launch_gram_partials_bf16(const void* kp, const void* vp, const float
 // and the readout fragments of M = W_q S for `frames` states per (b, h)
 // (fp32 row-major at states + (b*H + h)*sbh + n*sfr, in floats).
 hipError_t launch_gram_fmap(const float* partial, int nsplit, const void* wk, const void* wv, float* gram,
-                            const Shape& s, hipStream_t st);
+                            const Shape& s, hipStream_t st, unsigned* flags = nullptr);
 hipError_t launch_mfrag(const float* states, long long sbh, long long sfr, const void* wq, void* mfrag,
                         int frames, const Shape& s, hipStream_t st);
 // Step sizes for L2-normalised keys (fmap.hip): with n_t = ||K_t W_k||,

@@ -431,13 +431,15 @@ ha_status hybrid_attn_forward_mix(const void* q, const void* k, const void* v, c
 //   update_state = 1 : gram pass on K, V (fp32 partial sums), the transform to
 //                      the increments under the maps, the scan (fp32
 //                      snapshots S_{n-1}, S_F into `state`), M_n = W_q S_{n-1}
-//                      for every frame, then the readout on Q and M_n.
+//                      for every frame, then the readout on Q and M_n; with
+//                      more than 256 attention work-groups the scan runs in
+//                      the readout's launch and publishes M_n itself.
 // The gated variant (gates.hip) first computes alpha and beta from the layer
 // input x and, for normalised keys, the two step-size vectors beta / n^2 and
 // beta / n (keyscale), then runs the same passes.
 namespace {
 struct FmapWs {
-  size_t gram, partial, snaps, mfrag;
+  size_t gram, partial, snaps, mfrag, flags;
   size_t beta, beta_g, beta_b, apart, alpha;  // gated variant only
   size_t total;
 };
@@ -454,7 +456,8 @@ FmapWs fmap_layout(const ha::Shape& s, int update_state, bool gated) {
   w.partial = align_up(gf);
   w.snaps = w.partial + align_up(gf * ha::gram_splits(s));
   w.mfrag = w.snaps + align_up((size_t)s.B * s.H * s.F * dd * 4);
-  w.total = w.mfrag + align_up((size_t)s.B * s.H * s.F * dd * 2);
+  w.flags = w.mfrag + align_up((size_t)s.B * s.H * s.F * dd * 2);  // counters of the fused scan
+  w.total = w.flags + align_up((size_t)s.B * s.H * s.F * sizeof(unsigned));
   if (gated) {
     const size_t tok = (size_t)s.B * s.T * s.H * sizeof(float);
     w.beta = w.total;
@@ -484,6 +487,16 @@ ha_status fmap_run(const void* q, const void* k, const void* v, const void* wq, 
   void* mf = ws + lay.mfrag;
   const int nsplit = ha::gram_splits(s);
   if (ha::launch_gram_partials_bf16(k, v, beta, beta2, partial, nsplit, s, st) != hipSuccess) return HA_ERR_DEVICE;
+  if (ha::attn_groups(s) > ha::kAttnLoaderMaxGroups) {
+    // the scan runs in the readout's launch and publishes M_n = W_q S_{n-1}
+    // of every frame as its readout fragments (as the plain forward call does
+    // with S_{n-1}); the map transform zeroes the frame counters
+    unsigned* flags = (unsigned*)(ws + lay.flags);
+    if (ha::launch_gram_fmap(partial, nsplit, wk, wv, gram, s, st, flags) != hipSuccess) return HA_ERR_DEVICE;
+    const ha_status r =
+        launched(ha::launch_attn_scan_bf16(q, k, v, q, gram, alpha, state, mf, flags, out, s, scale, st, wq));
+    return r != HA_OK ? r : check_finite("state", state, (size_t)s.B * s.H * (size_t)dd, st);
+  }
   if (ha::launch_gram_fmap(partial, nsplit, wk, wv, gram, s, st) != hipSuccess) return HA_ERR_DEVICE;
   if (ha::launch_state_scan_bf16(gram, alpha, state, snaps, nullptr, s, st) != hipSuccess) return HA_ERR_DEVICE;
   if (ha::launch_mfrag(snaps, (long long)s.F * dd, dd, wq, mf, s.F, s, st) != hipSuccess) return HA_ERR_DEVICE;
