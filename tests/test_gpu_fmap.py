@@ -157,3 +157,53 @@ def test_fmap_480p_sampled_heads():
                 worst_o = max(worst_o, rel_err(got[0, r, h], ref[r]))
     say(f"fmap 480p: rel_err out {worst_o:.3e} state {worst_s:.3e}")
     assert worst_o < TOL_OUT and worst_s < TOL_STATE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fmap_fused_scan_parity_and_graph_replay(d):
+    """More than 256 attention work-groups: the scan runs in the readout's
+    launch and publishes the fragments of W_q S_{n-1} itself. Against the
+    oracle, then HIP-graph replays of the captured call (the map transform
+    zeroes the frame counters, so every replay starts clean) bitwise equal to
+    eager calls."""
+    w = small("480p", B=1, H=8, d=d, L=200, frames=17, state0_sigma=0.05)
+    assert w.B * w.H * w.frames * ((w.L + 127) // 128) > 256
+    say(f"case fmap, scan in the readout launch, d={d}")
+    eo, es, *_ = compare(w, 1)
+    say(f"  rel_err out {eo:.3e} state {es:.3e}")
+    assert eo < TOL_OUT and es < TOL_STATE
+    inp = W.make_call_inputs(w, 0, w.frames, 0, clean=True)
+    dev = upload(inp, w.dtype)
+    wdev, _ = maps(w)
+    s0 = torch.from_numpy(W.make_state0(w)).cuda()
+    out = torch.empty_like(dev["q"])
+    ws = torch.empty(api.fmap_workspace_bytes(1, w.H, w.T, w.L, w.d, 1), dtype=torch.uint8, device="cuda")
+
+    def call(state):
+        run_fmap(dev, wdev, state, w.L, 1, out=out, workspace=ws)
+
+    st = s0.clone()
+    ref = []
+    for _ in range(3):
+        call(st)
+        torch.cuda.synchronize()
+        ref.append((out.clone(), st.clone()))
+    gst = s0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(gst)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(gst)
+    torch.cuda.synchronize()
+    gst.copy_(s0)
+    for i in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[i][0]) and torch.equal(gst, ref[i][1])
+        junk = torch.randn(1 << 16, device="cuda").sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
