@@ -159,16 +159,16 @@ def test_fmap_480p_sampled_heads():
     assert worst_o < TOL_OUT and worst_s < TOL_STATE
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_fmap_fused_scan_parity_and_graph_replay(d):
+@pytest.mark.parametrize("d,B,H,L,F", [(64, 1, 8, 200, 17), (128, 1, 8, 200, 17), (128, 2, 12, 1560, 1)])
+def test_fmap_fused_scan_parity_and_graph_replay(d, B, H, L, F):
     """More than 256 attention work-groups: the scan runs in the readout's
     launch and publishes the fragments of W_q S_{n-1} itself. Against the
     oracle, then HIP-graph replays of the captured call (the map transform
     zeroes the frame counters, so every replay starts clean) bitwise equal to
     eager calls."""
-    w = small("480p", B=1, H=8, d=d, L=200, frames=17, state0_sigma=0.05)
+    w = small("480p", B=B, H=H, d=d, L=L, frames=F, state0_sigma=0.05)
     assert w.B * w.H * w.frames * ((w.L + 127) // 128) > 256
-    say(f"case fmap, scan in the readout launch, d={d}")
+    say(f"case fmap, scan in the readout launch, d={d} B={B} H={H} L={L} F={F}")
     eo, es, *_ = compare(w, 1)
     say(f"  rel_err out {eo:.3e} state {es:.3e}")
     assert eo < TOL_OUT and es < TOL_STATE
@@ -177,7 +177,7 @@ def test_fmap_fused_scan_parity_and_graph_replay(d):
     wdev, _ = maps(w)
     s0 = torch.from_numpy(W.make_state0(w)).cuda()
     out = torch.empty_like(dev["q"])
-    ws = torch.empty(api.fmap_workspace_bytes(1, w.H, w.T, w.L, w.d, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(api.fmap_workspace_bytes(w.B, w.H, w.T, w.L, w.d, 1), dtype=torch.uint8, device="cuda")
 
     def call(state):
         run_fmap(dev, wdev, state, w.L, 1, out=out, workspace=ws)
